@@ -109,15 +109,17 @@ def forward(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
     ``token_limit`` stops every sequence after that many of its tokens.
     Returns (o [B, T, Hv, dv] float64, final_state [N, Hv, dv, dk] float64).
     """
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    g = np.asarray(g, dtype=np.float64)
-    beta = np.asarray(beta, dtype=np.float64)
-    B, T, hk, dk = q.shape
-    hv, dv = v.shape[2], v.shape[3]
+    B, T, hk, dk = np.shape(q)
+    hv, dv = np.shape(v)[2], np.shape(v)[3]
     kmap = head_map(hk, hv)
     hs = np.arange(hv) if heads is None else np.asarray(heads, dtype=np.int64)
+    # only the value heads asked for, and the key heads they read, are upcast
+    kh = kmap[hs]
+    q = np.asarray(np.asarray(q)[:, :, kh], dtype=np.float64)
+    k = np.asarray(np.asarray(k)[:, :, kh], dtype=np.float64)
+    v = np.asarray(np.asarray(v)[:, :, hs], dtype=np.float64)
+    g = np.asarray(np.asarray(g)[:, :, hs], dtype=np.float64)
+    beta = np.asarray(np.asarray(beta)[:, :, hs], dtype=np.float64)
     if use_qk_l2norm:
         q = l2_normalise(q, eps)
         k = l2_normalise(k, eps)
@@ -130,8 +132,7 @@ def forward(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *,
         S0 = np.zeros((len(hs), dv, dk)) if initial_state is None else \
             np.asarray(initial_state[n], dtype=np.float64)[hs]
         sl = slice(t0, t1)
-        o_seq, S = recurrence(S0, np.exp(g[b, sl][:, hs]), beta[b, sl][:, hs],
-                              k[b, sl][:, kmap[hs]], v[b, sl][:, hs], q[b, sl][:, kmap[hs]], scale)
+        o_seq, S = recurrence(S0, np.exp(g[b, sl]), beta[b, sl], k[b, sl], v[b, sl], q[b, sl], scale)
         o[b, sl][:, hs] = o_seq
         final[n, hs] = S
     return o, final
