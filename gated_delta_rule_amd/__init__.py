@@ -1,0 +1,22 @@
+"""Gated delta rule for AMD MI355X (gfx950): HIP kernels behind a C ABI.
+
+The compute lives in libgdr.so (include/gdr.h); this package is a thin torch
+binding over it.  Importing the ops loads the library and raises ImportError
+if it has not been built (``python -m gated_delta_rule_amd.build``).
+"""
+from ._lib import GDRError, load as load_library  # noqa: F401
+from .ops import (  # noqa: F401
+    chunk_gated_delta_rule,
+    conv_gate_fused,
+    gated_rmsnorm,
+    recurrent_step,
+)
+
+__all__ = [
+    "GDRError",
+    "load_library",
+    "chunk_gated_delta_rule",
+    "recurrent_step",
+    "conv_gate_fused",
+    "gated_rmsnorm",
+]

@@ -1,0 +1,118 @@
+"""ctypes view of libgdr.so (include/gdr.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation of any entry point.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdr.so")
+
+GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_HIP = 0, -1, -2, -3
+GDR_F32, GDR_BF16 = 0, 1
+
+EXPORTED = (
+    "gdr_abi_version",
+    "gdr_status_string",
+    "gdr_last_error",
+    "gdr_chunk_fwd_workspace_size",
+    "gdr_chunk_fwd",
+    "gdr_recurrent_step",
+    "gdr_conv_gate_fused",
+    "gdr_gated_rmsnorm",
+)
+
+
+class GdrDesc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("batch", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("num_k_heads", ctypes.c_int32),
+        ("num_v_heads", ctypes.c_int32),
+        ("head_dim_k", ctypes.c_int32),
+        ("head_dim_v", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32),
+        ("qkv_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("use_qk_l2norm", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("l2norm_eps", ctypes.c_float),
+    ]
+
+
+class GdrConvDesc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("num_tokens", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("num_k_heads", ctypes.c_int32),
+        ("num_v_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+    ]
+
+
+class GdrNormDesc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("num_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("o_dtype", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+    ]
+
+
+class GDRError(RuntimeError):
+    """A libgdr entry point returned a negative status."""
+
+    def __init__(self, func: str, status: int, message: str):
+        super().__init__(f"{func} failed with {status_string(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgdr.so (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_amd.build` "
+            "(hipcc, gfx950). There is no non-HIP implementation of this library.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.gdr_abi_version.restype = I32
+    lib.gdr_abi_version.argtypes = []
+    lib.gdr_status_string.restype = ctypes.c_char_p
+    lib.gdr_status_string.argtypes = [I32]
+    lib.gdr_last_error.restype = ctypes.c_char_p
+    lib.gdr_last_error.argtypes = []
+    lib.gdr_chunk_fwd_workspace_size.restype = I32
+    lib.gdr_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.POINTER(SZ)]
+    lib.gdr_chunk_fwd.restype = I32
+    lib.gdr_chunk_fwd.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.gdr_recurrent_step.restype = I32
+    lib.gdr_recurrent_step.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, P, P]
+    lib.gdr_conv_gate_fused.restype = I32
+    lib.gdr_conv_gate_fused.argtypes = [ctypes.POINTER(GdrConvDesc)] + [P] * 15
+    lib.gdr_gated_rmsnorm.restype = I32
+    lib.gdr_gated_rmsnorm.argtypes = [ctypes.POINTER(GdrNormDesc), P, P, P, P, P]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gdr_status_string(status).decode()
+
+
+def check(func: str, status: int) -> None:
+    if status != GDR_OK:
+        raise GDRError(func, status, load().gdr_last_error().decode())

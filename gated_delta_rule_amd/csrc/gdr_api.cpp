@@ -1,0 +1,245 @@
+// C ABI of libgdr: argument validation and kernel dispatch.  Every check runs
+// on the host before anything is enqueued; no entry point allocates, frees or
+// synchronises.  See include/gdr.h for the contract of each call.
+#include "gdr.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gdr_status fail(gdr_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gdr_status ok() {
+  g_last_error.clear();
+  return GDR_OK;
+}
+
+gdr_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(GDR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int32_t t) { return t == GDR_F32 || t == GDR_BF16; }
+
+bool supported_dim(int32_t d) { return d == 32 || d == 64 || d == 128; }
+
+// Shape/option checks shared by gdr_chunk_fwd and gdr_recurrent_step.
+gdr_status check_desc(const gdr_desc* d, bool decode, bool has_cu) {
+  if (!d) return fail(GDR_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->struct_size < sizeof(gdr_desc))
+    return fail(GDR_ERR_INVALID_ARG, "descriptor struct_size %u < %zu", d->struct_size, sizeof(gdr_desc));
+  if (d->batch < 0 || d->seq_len < 0 || d->num_seqs < 0)
+    return fail(GDR_ERR_INVALID_ARG, "negative batch/seq_len/num_seqs");
+  if (d->num_k_heads <= 0 || d->num_v_heads <= 0)
+    return fail(GDR_ERR_INVALID_ARG, "head counts must be positive");
+  if (d->num_v_heads % d->num_k_heads)
+    return fail(GDR_ERR_INVALID_ARG, "num_v_heads (%d) must be a multiple of num_k_heads (%d)", d->num_v_heads,
+                d->num_k_heads);
+  if (!valid_dtype(d->qkv_dtype) || !valid_dtype(d->out_dtype))
+    return fail(GDR_ERR_INVALID_ARG, "unknown dtype code");
+  if (!(d->l2norm_eps >= 0.f) || !std::isfinite(d->scale))
+    return fail(GDR_ERR_INVALID_ARG, "l2norm_eps must be >= 0 and scale finite");
+  if (d->head_dim_k != d->head_dim_v || !supported_dim(d->head_dim_k))
+    return fail(GDR_ERR_UNSUPPORTED, "head dims %d/%d: need d_k == d_v in {32, 64, 128}", d->head_dim_k,
+                d->head_dim_v);
+  if (decode) {
+    if (d->seq_len != 1) return fail(GDR_ERR_INVALID_ARG, "decode needs seq_len == 1");
+    if (d->num_seqs != d->batch) return fail(GDR_ERR_INVALID_ARG, "decode needs num_seqs == batch");
+  } else {
+    if (d->chunk_size != 64 && d->chunk_size != 32)
+      return fail(GDR_ERR_UNSUPPORTED, "chunk_size %d: need 32 or 64", d->chunk_size);
+    if (has_cu) {
+      if (d->batch != 1) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens needs batch == 1");
+    } else if (d->num_seqs != d->batch) {
+      return fail(GDR_ERR_INVALID_ARG, "without cu_seqlens num_seqs must equal batch");
+    }
+  }
+  const double tokens = (double)d->batch * d->seq_len;
+  if (tokens * d->num_v_heads * d->head_dim_v >= 9.0e18)
+    return fail(GDR_ERR_INVALID_ARG, "problem too large");
+  return GDR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdr_abi_version(void) { return GDR_ABI_VERSION; }
+
+const char* gdr_status_string(int status) {
+  switch (status) {
+    case GDR_OK: return "GDR_OK";
+    case GDR_ERR_INVALID_ARG: return "GDR_ERR_INVALID_ARG";
+    case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED";
+    case GDR_ERR_HIP: return "GDR_ERR_HIP";
+    default: return "GDR_UNKNOWN_STATUS";
+  }
+}
+
+const char* gdr_last_error(void) { return g_last_error.c_str(); }
+
+gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* d, size_t* bytes) {
+  if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+  // a packed batch (cu_seqlens) is the only way num_seqs can differ from batch
+  gdr_status st = check_desc(d, false, d && d->num_seqs != d->batch);
+  if (st != GDR_OK) return st;
+  *bytes = 0;
+  return ok();
+}
+
+gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, float* final_state,
+                         const int32_t* cu_seqlens, void* o, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  gdr_status st = check_desc(d, false, cu_seqlens != nullptr);
+  if (st != GDR_OK) return st;
+  const long long tokens = (long long)d->batch * d->seq_len;
+  if (tokens > 0 && (!q || !k || !v || !g || !beta || !o))
+    return fail(GDR_ERR_INVALID_ARG, "q, k, v, g, beta and o are required");
+  if (cu_seqlens == nullptr && d->num_seqs > 0 && d->seq_len == 0 && !final_state) return ok();
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(initial_state) ||
+      !aligned16(final_state))
+    return fail(GDR_ERR_INVALID_ARG, "q, k, v, o and state pointers must be 16-byte aligned");
+  if (d->num_seqs == 0) return ok();
+  gdr::ChunkArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.initial_state = initial_state;
+  a.final_state = final_state;
+  a.cu_seqlens = cu_seqlens;
+  a.o = o;
+  a.N = d->num_seqs;
+  a.T = d->seq_len;
+  a.Hk = d->num_k_heads;
+  a.Hv = d->num_v_heads;
+  a.D = d->head_dim_k;
+  a.C = d->chunk_size;
+  a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
+  a.out_bf16 = d->out_dtype == GDR_BF16;
+  a.use_l2 = d->use_qk_l2norm != 0;
+  a.scale = d->scale;
+  a.eps = d->l2norm_eps;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool mfma = a.qkv_bf16 && a.D == 128 && a.C == 64;
+  return hip_status(mfma ? gdr::launch_chunk_bf16(a, s) : gdr::launch_chunk_f32(a, s), "gdr_chunk_fwd launch");
+}
+
+gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, float* state, void* o, void* stream) {
+  gdr_status st = check_desc(d, true, false);
+  if (st != GDR_OK) return st;
+  if (d->batch == 0) return ok();
+  if (!q || !k || !v || !g || !beta || !state || !o)
+    return fail(GDR_ERR_INVALID_ARG, "q, k, v, g, beta, state and o are required");
+  if (!aligned16(state)) return fail(GDR_ERR_INVALID_ARG, "state must be 16-byte aligned");
+  gdr::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.N = d->batch;
+  a.Hk = d->num_k_heads;
+  a.Hv = d->num_v_heads;
+  a.D = d->head_dim_k;
+  a.qkv_bf16 = d->qkv_dtype == GDR_BF16;
+  a.out_bf16 = d->out_dtype == GDR_BF16;
+  a.use_l2 = d->use_qk_l2norm != 0;
+  a.scale = d->scale;
+  a.eps = d->l2norm_eps;
+  return hip_status(gdr::launch_decode(a, static_cast<hipStream_t>(stream)), "gdr_recurrent_step launch");
+}
+
+gdr_status gdr_conv_gate_fused(const gdr_conv_desc* d, const void* x, const void* conv_w,
+                               const int32_t* cu_seqlens, const void* conv_state_in, void* conv_state_out,
+                               const float* a, const float* b, const float* A_log, const float* dt_bias,
+                               void* q_out, void* k_out, void* v_out, float* g, float* beta, void* stream) {
+  if (!d) return fail(GDR_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->struct_size < sizeof(gdr_conv_desc))
+    return fail(GDR_ERR_INVALID_ARG, "descriptor struct_size %u < %zu", d->struct_size, sizeof(gdr_conv_desc));
+  if (d->num_tokens < 0 || d->num_seqs < 1 || d->num_k_heads <= 0 || d->num_v_heads <= 0)
+    return fail(GDR_ERR_INVALID_ARG, "need num_tokens >= 0, num_seqs >= 1, positive head counts");
+  if (!supported_dim(d->head_dim)) return fail(GDR_ERR_UNSUPPORTED, "head_dim %d: need 32, 64 or 128", d->head_dim);
+  if (!cu_seqlens) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens is required");
+  if (d->num_tokens > 0 &&
+      (!x || !conv_w || !a || !b || !A_log || !dt_bias || !q_out || !k_out || !v_out || !g || !beta))
+    return fail(GDR_ERR_INVALID_ARG, "x, conv_w, a, b, A_log, dt_bias and all outputs are required");
+  if (conv_state_out && conv_state_out == conv_state_in)
+    return fail(GDR_ERR_INVALID_ARG, "conv_state_out must not alias conv_state_in");
+  if (!aligned16(x) || !aligned16(conv_w) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(v_out))
+    return fail(GDR_ERR_INVALID_ARG, "x, conv_w and q/k/v outputs must be 16-byte aligned");
+  gdr::ConvArgs c{};
+  c.x = x;
+  c.w = conv_w;
+  c.cu_seqlens = cu_seqlens;
+  c.state_in = conv_state_in;
+  c.state_out = conv_state_out;
+  c.a = a;
+  c.b = b;
+  c.A_log = A_log;
+  c.dt_bias = dt_bias;
+  c.q_out = q_out;
+  c.k_out = k_out;
+  c.v_out = v_out;
+  c.g = g;
+  c.beta = beta;
+  c.T = d->num_tokens;
+  c.N = d->num_seqs;
+  c.Hk = d->num_k_heads;
+  c.Hv = d->num_v_heads;
+  c.D = d->head_dim;
+  return hip_status(gdr::launch_conv_front(c, static_cast<hipStream_t>(stream)), "gdr_conv_gate_fused launch");
+}
+
+gdr_status gdr_gated_rmsnorm(const gdr_norm_desc* d, const void* o, const void* z, const float* w, void* y,
+                             void* stream) {
+  if (!d) return fail(GDR_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->struct_size < sizeof(gdr_norm_desc))
+    return fail(GDR_ERR_INVALID_ARG, "descriptor struct_size %u < %zu", d->struct_size, sizeof(gdr_norm_desc));
+  if (d->num_tokens < 0 || d->num_heads <= 0) return fail(GDR_ERR_INVALID_ARG, "bad num_tokens/num_heads");
+  if (!valid_dtype(d->o_dtype)) return fail(GDR_ERR_INVALID_ARG, "unknown dtype code");
+  if (!(d->eps >= 0.f)) return fail(GDR_ERR_INVALID_ARG, "eps must be >= 0");
+  if (!supported_dim(d->head_dim)) return fail(GDR_ERR_UNSUPPORTED, "head_dim %d: need 32, 64 or 128", d->head_dim);
+  if (d->num_tokens > 0 && (!o || !z || !w || !y)) return fail(GDR_ERR_INVALID_ARG, "o, z, w and y are required");
+  if (!aligned16(o) || !aligned16(z) || !aligned16(y) || !aligned16(w))
+    return fail(GDR_ERR_INVALID_ARG, "o, z, w and y must be 16-byte aligned");
+  gdr::NormArgs n{};
+  n.o = o;
+  n.z = z;
+  n.w = w;
+  n.y = y;
+  n.T = d->num_tokens;
+  n.H = d->num_heads;
+  n.D = d->head_dim;
+  n.o_bf16 = d->o_dtype == GDR_BF16;
+  n.eps = d->eps;
+  return hip_status(gdr::launch_gated_rmsnorm(n, static_cast<hipStream_t>(stream)), "gdr_gated_rmsnorm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Launch interface between the C ABI (gdr_api.cpp) and the kernels.  Every
+// launcher assumes its arguments were validated by the ABI layer and only
+// enqueues work on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdr {
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  float* state;
+  void* o;
+  int N, Hk, Hv, D;
+  int qkv_bf16, out_bf16, use_l2;
+  float scale, eps;
+};
+
+struct ChunkArgs {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  const float* initial_state;
+  float* final_state;
+  const int32_t* cu_seqlens;  // NULL: N rows of T tokens
+  void* o;
+  int N, T, Hk, Hv, D, C;     // T: tokens per row (or packed total)
+  int qkv_bf16, out_bf16, use_l2;
+  float scale, eps;
+};
+
+struct ConvArgs {
+  const void *x, *w;
+  const int32_t* cu_seqlens;
+  const void* state_in;
+  void* state_out;
+  const float *a, *b, *A_log, *dt_bias;
+  void *q_out, *k_out, *v_out;
+  float *g, *beta;
+  int T, N, Hk, Hv, D;
+};
+
+struct NormArgs {
+  const void* o;
+  const void* z;
+  const float* w;
+  void* y;
+  int T, H, D, o_bf16;
+  float eps;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t st);
+hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t st);
+hipError_t launch_conv_front(const ConvArgs& a, hipStream_t st);
+hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t st);
+
+}  // namespace gdr

@@ -1,0 +1,213 @@
+"""Torch-facing wrappers of the libgdr entry points.
+
+Each function checks tensor placement, dtype and contiguity, allocates its
+outputs with torch, and passes raw device pointers and the current HIP stream
+to the C ABI.  Every step of the computation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.GDR_F32, torch.bfloat16: _lib.GDR_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtypes, device) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_desc(B, T, N, Hk, Hv, D, chunk_size, qkv_dtype, out_dtype, use_qk_l2norm, scale, eps):
+    d = _lib.GdrDesc()
+    d.struct_size = ctypes.sizeof(_lib.GdrDesc)
+    d.batch, d.seq_len, d.num_seqs = B, T, N
+    d.num_k_heads, d.num_v_heads = Hk, Hv
+    d.head_dim_k = d.head_dim_v = D
+    d.chunk_size = chunk_size
+    d.qkv_dtype = _DT[qkv_dtype]
+    d.out_dtype = _DT[out_dtype]
+    d.use_qk_l2norm = int(bool(use_qk_l2norm))
+    d.scale = scale
+    d.l2norm_eps = eps
+    return d
+
+
+def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                           beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                           output_final_state: bool = False, cu_seqlens: Optional[torch.Tensor] = None,
+                           use_qk_l2norm_in_kernel: bool = True, scale: float = 1.0,
+                           chunk_size: int = 64, out_dtype: torch.dtype = torch.float32,
+                           final_state: Optional[torch.Tensor] = None,
+                           out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill (gdr_chunk_fwd).
+
+    q, k: [B, T, Hk, d]; v: [B, T, Hv, d] (bf16 or fp32, same dtype);
+    g, beta: [B, T, Hv] fp32; initial_state: [N, Hv, d, d] fp32 or None;
+    cu_seqlens: int32 [N+1] (then B must be 1).  ``final_state`` may be given
+    as a preallocated output (it may be ``initial_state`` itself).
+    Returns (o [B, T, Hv, d] out_dtype, final_state or None).
+    """
+    dev = q.device
+    qd = q.dtype
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, (qd,), dev)
+    if qd not in _DT:
+        raise TypeError(f"q/k/v dtype {qd} unsupported")
+    _need(g, "g", (torch.float32,), dev)
+    _need(beta, "beta", (torch.float32,), dev)
+    B, T, Hk, D = q.shape
+    Hv = v.shape[2]
+    if k.shape != q.shape or v.shape != (B, T, Hv, D) or g.shape != (B, T, Hv) or beta.shape != (B, T, Hv):
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (torch.int32,), dev)
+        N = cu_seqlens.numel() - 1
+        if B != 1:
+            raise ValueError("cu_seqlens needs B == 1")
+    else:
+        N = B
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (torch.float32,), dev)
+        if initial_state.shape != (N, Hv, D, D):
+            raise ValueError(f"initial_state must be {(N, Hv, D, D)}")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, Hv, D, D), device=dev, dtype=torch.float32)
+    if final_state is not None:
+        _need(final_state, "final_state", (torch.float32,), dev)
+        if final_state.shape != (N, Hv, D, D):
+            raise ValueError(f"final_state must be {(N, Hv, D, D)}")
+    if out is None:
+        out = torch.empty((B, T, Hv, D), device=dev, dtype=out_dtype)
+    else:
+        _need(out, "out", (out_dtype,), dev)
+    desc = make_desc(B, T, N, Hk, Hv, D, chunk_size, qd, out_dtype, use_qk_l2norm_in_kernel, scale, 1e-6)
+    lib = _lib.load()
+    st = lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                           _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(out),
+                           None, 0, _stream(dev))
+    _lib.check("gdr_chunk_fwd", st)
+    return out, final_state
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+                   state: torch.Tensor, use_qk_l2norm_in_kernel: bool = True, scale: float = 1.0,
+                   out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode token (gdr_recurrent_step); ``state`` [N, Hv, d, d] is updated in place.
+
+    q, k: [N, Hk, d]; v: [N, Hv, d]; g, beta: [N, Hv] fp32.  Returns o [N, Hv, d].
+    """
+    dev = q.device
+    qd = q.dtype
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, (qd,), dev)
+    if qd not in _DT:
+        raise TypeError(f"q/k/v dtype {qd} unsupported")
+    _need(g, "g", (torch.float32,), dev)
+    _need(beta, "beta", (torch.float32,), dev)
+    _need(state, "state", (torch.float32,), dev)
+    N, Hk, D = q.shape
+    Hv = v.shape[1]
+    if k.shape != q.shape or v.shape != (N, Hv, D) or g.shape != (N, Hv) or beta.shape != (N, Hv) \
+            or state.shape != (N, Hv, D, D):
+        raise ValueError("shape mismatch among q, k, v, g, beta, state")
+    if out is None:
+        out = torch.empty((N, Hv, D), device=dev, dtype=out_dtype)
+    else:
+        _need(out, "out", (out_dtype,), dev)
+    desc = make_desc(N, 1, N, Hk, Hv, D, 64, qd, out_dtype, use_qk_l2norm_in_kernel, scale, 1e-6)
+    st = _lib.load().gdr_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                        _ptr(state), _ptr(out), _stream(dev))
+    _lib.check("gdr_recurrent_step", st)
+    return out
+
+
+def conv_gate_fused(x: torch.Tensor, conv_w: torch.Tensor, cu_seqlens: torch.Tensor, a: torch.Tensor,
+                    b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor, num_k_heads: int,
+                    num_v_heads: int, head_dim: int, conv_state_in: Optional[torch.Tensor] = None,
+                    output_conv_state: bool = False):
+    """Conv + SiLU + gates front (gdr_conv_gate_fused).
+
+    x: [T, C] bf16 with C = 2*Hk*d + Hv*d; conv_w: [C, 4] bf16; cu_seqlens int32 [N+1];
+    a, b: [T, Hv] fp32; A_log, dt_bias: [Hv] fp32.
+    Returns (q [1, T, Hk, d], k [1, T, Hk, d], v [1, T, Hv, d], g [1, T, Hv], beta [1, T, Hv],
+    conv_state_out [N, C, 3] or None).
+    """
+    dev = x.device
+    Hk, Hv, D = num_k_heads, num_v_heads, head_dim
+    T, C = x.shape
+    if C != (2 * Hk + Hv) * D:
+        raise ValueError("x width must be 2*Hk*d + Hv*d")
+    _need(x, "x", (torch.bfloat16,), dev)
+    _need(conv_w, "conv_w", (torch.bfloat16,), dev)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,), dev)
+    for t, name in ((a, "a"), (b, "b"), (A_log, "A_log"), (dt_bias, "dt_bias")):
+        _need(t, name, (torch.float32,), dev)
+    if conv_w.shape != (C, 4) or a.shape != (T, Hv) or b.shape != (T, Hv) or A_log.shape != (Hv,) \
+            or dt_bias.shape != (Hv,):
+        raise ValueError("shape mismatch in conv front inputs")
+    N = cu_seqlens.numel() - 1
+    if conv_state_in is not None:
+        _need(conv_state_in, "conv_state_in", (torch.bfloat16,), dev)
+        if conv_state_in.shape != (N, C, 3):
+            raise ValueError(f"conv_state_in must be {(N, C, 3)}")
+    q = torch.empty((1, T, Hk, D), device=dev, dtype=torch.bfloat16)
+    k = torch.empty((1, T, Hk, D), device=dev, dtype=torch.bfloat16)
+    v = torch.empty((1, T, Hv, D), device=dev, dtype=torch.bfloat16)
+    g = torch.empty((1, T, Hv), device=dev, dtype=torch.float32)
+    beta = torch.empty((1, T, Hv), device=dev, dtype=torch.float32)
+    state_out = torch.empty((N, C, 3), device=dev, dtype=torch.bfloat16) if output_conv_state else None
+    desc = _lib.GdrConvDesc()
+    desc.struct_size = ctypes.sizeof(_lib.GdrConvDesc)
+    desc.num_tokens, desc.num_seqs = T, N
+    desc.num_k_heads, desc.num_v_heads, desc.head_dim = Hk, Hv, D
+    st = _lib.load().gdr_conv_gate_fused(ctypes.byref(desc), _ptr(x), _ptr(conv_w), _ptr(cu_seqlens),
+                                         _ptr(conv_state_in), _ptr(state_out), _ptr(a), _ptr(b), _ptr(A_log),
+                                         _ptr(dt_bias), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                         _stream(dev))
+    _lib.check("gdr_conv_gate_fused", st)
+    return q, k, v, g, beta, state_out
+
+
+def gated_rmsnorm(o: torch.Tensor, z: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gated RMSNorm back (gdr_gated_rmsnorm).
+
+    o: [..., Hv, d] fp32 or bf16; z: [..., Hv*d] bf16 (same leading size);
+    w: [d] fp32.  Returns y [..., Hv*d] bf16.
+    """
+    dev = o.device
+    _need(o, "o", (torch.float32, torch.bfloat16), dev)
+    _need(z, "z", (torch.bfloat16,), dev)
+    _need(w, "w", (torch.float32,), dev)
+    Hv, D = o.shape[-2], o.shape[-1]
+    T = o.numel() // (Hv * D)
+    if z.numel() != T * Hv * D or w.shape != (D,):
+        raise ValueError("shape mismatch among o, z, w")
+    if out is None:
+        out = torch.empty(z.shape, device=dev, dtype=torch.bfloat16)
+    desc = _lib.GdrNormDesc()
+    desc.struct_size = ctypes.sizeof(_lib.GdrNormDesc)
+    desc.num_tokens, desc.num_heads, desc.head_dim = T, Hv, D
+    desc.o_dtype = _DT[o.dtype]
+    desc.eps = eps
+    st = _lib.load().gdr_gated_rmsnorm(ctypes.byref(desc), _ptr(o), _ptr(z), _ptr(w), _ptr(out), _stream(dev))
+    _lib.check("gdr_gated_rmsnorm", st)
+    return out

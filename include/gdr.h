@@ -1,0 +1,200 @@
+/*
+ * gdr.h -- C ABI of the gated delta rule library (libgdr.so) for AMD MI355X (gfx950).
+ *
+ * The library computes the hot path of a gated delta rule layer as the
+ * Agnes-3.0-Flash pages describe it: per (sequence, value head) an fp32 state
+ * S in R^{d_v x d_k} updated token by token as
+ *
+ *     S_t = S_{t-1} * exp(g_t) * (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = scale * S_t q_t
+ *
+ * (gpts24 page: the delta-rule update in words and the gated variant's forget
+ * gate; yfxerp page, section 1.2: the recurrent call with g, beta, an initial
+ * state, an optional final state and q/k L2 normalisation inside the kernel,
+ * a chunk_size=64 block-parallel prefill and a single-step decode; deepmagic
+ * page, architecture section: 16 key heads / 48 value heads of dim 128, a
+ * kernel-4 causal conv in front, a gated RMS norm behind, an fp32 state).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers, owned by the caller, contiguous
+ *     in the layout documented per argument and 16-byte aligned.  Descriptor
+ *     and size arguments are HOST pointers.
+ *   - The library allocates nothing, frees nothing and never synchronises:
+ *     every kernel is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns immediately.
+ *   - Argument errors are reported synchronously, before anything is
+ *     enqueued, as a negative gdr_status; gdr_last_error() then returns a
+ *     thread-local message.  Device-side faults surface at the caller's next
+ *     synchronisation.  Device array CONTENTS (e.g. cu_seqlens) are trusted.
+ *   - Value head h reads key head h / (Hv / Hk) (contiguous groups).
+ *   - Thread safety: calls from several host threads are safe; kernels that
+ *     write the same output buffers concurrently race, as usual.
+ */
+#ifndef GDR_H_
+#define GDR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDR_ABI_VERSION 1
+
+typedef enum gdr_status {
+  GDR_OK = 0,
+  GDR_ERR_INVALID_ARG = -1, /* NULL where required, bad shape, misalignment, short workspace */
+  GDR_ERR_UNSUPPORTED = -2, /* valid but not implemented: head dim, chunk size, dtype combination */
+  GDR_ERR_HIP = -3          /* a HIP runtime error while enqueueing (launch failure) */
+} gdr_status;
+
+typedef enum gdr_dtype { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+/* Shape and options of the recurrence (gdr_chunk_fwd, gdr_recurrent_step). */
+typedef struct gdr_desc {
+  uint32_t struct_size; /* sizeof(gdr_desc) */
+  int32_t batch;        /* B rows; must be 1 when cu_seqlens is given */
+  int32_t seq_len;      /* T tokens per row (packed total with cu_seqlens); 1 for decode */
+  int32_t num_seqs;     /* N sequences: B without cu_seqlens, else length of cu_seqlens - 1 */
+  int32_t num_k_heads;  /* Hk */
+  int32_t num_v_heads;  /* Hv, a multiple of Hk */
+  int32_t head_dim_k;   /* d_k */
+  int32_t head_dim_v;   /* d_v */
+  int32_t chunk_size;   /* C: 64 or 32 (prefill only) */
+  int32_t qkv_dtype;    /* gdr_dtype of q, k, v */
+  int32_t out_dtype;    /* gdr_dtype of o */
+  int32_t use_qk_l2norm; /* nonzero: q, k <- x / sqrt(sum(x^2) + l2norm_eps) per token and key head */
+  float scale;          /* output scale (1.0 reproduces o_t = S_t q_t) */
+  float l2norm_eps;     /* 1e-6 by convention */
+} gdr_desc;
+
+/* Shape of the conv + gate front (gdr_conv_gate_fused). */
+typedef struct gdr_conv_desc {
+  uint32_t struct_size; /* sizeof(gdr_conv_desc) */
+  int32_t num_tokens;   /* T, packed over all sequences */
+  int32_t num_seqs;     /* N = length of cu_seqlens - 1 */
+  int32_t num_k_heads;  /* Hk */
+  int32_t num_v_heads;  /* Hv */
+  int32_t head_dim;     /* d (= d_k = d_v); channels C = 2*Hk*d + Hv*d */
+} gdr_conv_desc;
+
+/* Shape of the gated RMSNorm back (gdr_gated_rmsnorm). */
+typedef struct gdr_norm_desc {
+  uint32_t struct_size; /* sizeof(gdr_norm_desc) */
+  int32_t num_tokens;   /* T */
+  int32_t num_heads;    /* Hv */
+  int32_t head_dim;     /* d_v: the normalised group */
+  int32_t o_dtype;      /* gdr_dtype of o */
+  float eps;            /* 1e-6 by convention */
+} gdr_norm_desc;
+
+/* Version of this ABI (GDR_ABI_VERSION of the built library). */
+int gdr_abi_version(void);
+
+/* Static name of a status code. */
+const char* gdr_status_string(int status);
+
+/* Message describing the last failed call on the calling thread ("" if none). */
+const char* gdr_last_error(void);
+
+/*
+ * Device workspace that gdr_chunk_fwd needs for descriptor *d, in bytes
+ * (currently 0 for every supported shape; callers may then pass NULL).
+ * Errors: INVALID_ARG / UNSUPPORTED as gdr_chunk_fwd would report them.
+ */
+gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* d, size_t* bytes);
+
+/*
+ * Chunked prefill (the pages' chunk_size=64 block-parallel path; the chunk
+ * form is an exact rewrite of the token recurrence above).
+ *
+ *   q, k          [B, T, Hk, d_k]  qkv_dtype
+ *   v             [B, T, Hv, d_v]  qkv_dtype
+ *   g             [B, T, Hv] fp32  log-decay (exp(g) multiplies the state)
+ *   beta          [B, T, Hv] fp32  write strength
+ *   initial_state [N, Hv, d_v, d_k] fp32, d_k contiguous; NULL = zero state
+ *   final_state   [N, Hv, d_v, d_k] fp32 output; NULL = not written.  May be
+ *                 the same pointer as initial_state (updated in place).
+ *   cu_seqlens    [N+1] int32 device array, cu[0] = 0, non-decreasing,
+ *                 cu[N] = T; sequence n is tokens [cu[n], cu[n+1]) of the
+ *                 single packed row.  NULL = B independent rows of T tokens.
+ *   o             [B, T, Hv, d_v]  out_dtype output (never aliases inputs)
+ *   workspace     device buffer of gdr_chunk_fwd_workspace_size() bytes
+ *
+ * Supported: d_k = d_v in {32, 64, 128}; chunk_size 64 or 32; qkv bf16 with
+ * d = 128 and chunk 64 takes the bf16-MFMA path, every other supported
+ * combination the fp32 path.  Chunks restart at every sequence start, so a
+ * packed batch gives results bit-identical to separate calls; a zero-length
+ * sequence copies its initial state to final_state.
+ */
+gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, const float* initial_state,
+                         float* final_state, const int32_t* cu_seqlens, void* o,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode token for N independent sequences (the pages' single-step
+ * fused recurrent path).  d->batch = N, d->seq_len = 1, cu_seqlens unused.
+ *
+ *   q, k   [N, Hk, d_k] qkv_dtype;  v [N, Hv, d_v] qkv_dtype
+ *   g, beta [N, Hv] fp32
+ *   state  [N, Hv, d_v, d_k] fp32, read and overwritten IN PLACE with S_t
+ *   o      [N, Hv, d_v] out_dtype
+ *
+ * Supported: d_k = d_v in {32, 64, 128}.
+ */
+gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, float* state, void* o,
+                              void* stream);
+
+/*
+ * Front of the layer: depthwise causal conv (kernel 4, no bias) + SiLU over
+ * all C = 2*Hk*d + Hv*d channels, plus the gates (deepmagic page: kernel-4
+ * causal conv in front; yfxerp page, section 1.2: beta = sigmoid(b),
+ * g = -exp(A_log) * softplus(a + dt_bias) in fp32).
+ *
+ *   x             [T, C] bf16, channel blocks q | k | v, each head-major
+ *   conv_w        [C, 4] bf16; tap 3 multiplies the current token, taps
+ *                 0..2 the three previous tokens of the same sequence
+ *   cu_seqlens    [N+1] int32 device array (required; N = 1 for one sequence)
+ *   conv_state_in [N, C, 3] bf16 history before each sequence, oldest first;
+ *                 NULL = zeros
+ *   conv_state_out[N, C, 3] bf16: the last three inputs of every sequence
+ *                 (history included); NULL = not written; must not alias
+ *                 conv_state_in
+ *   a, b          [T, Hv] fp32 raw projections;  A_log, dt_bias [Hv] fp32
+ *   q_out, k_out  [T, Hk, d] bf16;  v_out [T, Hv, d] bf16
+ *   g, beta       [T, Hv] fp32 outputs
+ *
+ * The bf16 outputs are bit-exact with this fixed evaluation: p_j = w_j*x_j in
+ * fp32 (exact for bf16 operands), acc = ((p0 + p1) + p2) + p3 with each add
+ * rounded to fp32, y = acc / (1 + exp32(-acc)) with exp32 the Cody-Waite /
+ * degree-7 Taylor exponential evaluated one IEEE fp32 operation at a time,
+ * then round to nearest-even bf16.  g and beta are fp32 (not bit-exact).
+ */
+gdr_status gdr_conv_gate_fused(const gdr_conv_desc* d, const void* x, const void* conv_w,
+                               const int32_t* cu_seqlens, const void* conv_state_in,
+                               void* conv_state_out, const float* a, const float* b,
+                               const float* A_log, const float* dt_bias, void* q_out,
+                               void* k_out, void* v_out, float* g, float* beta, void* stream);
+
+/*
+ * Back of the layer: gated RMS norm per (token, head) over d_v (deepmagic
+ * page: gated RMS norm after the recurrence; yfxerp page: z is Hv*d_v wide):
+ *
+ *   y = o / sqrt(mean(o^2) + eps) * w * z * sigmoid(z)
+ *
+ *   o  [T, Hv, d_v] o_dtype;  z [T, Hv*d_v] bf16;  w [d_v] fp32
+ *   y  [T, Hv*d_v] bf16
+ *
+ * Supported: d_v in {32, 64, 128}.
+ */
+gdr_status gdr_gated_rmsnorm(const gdr_norm_desc* d, const void* o, const void* z,
+                             const float* w, void* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H_ */

@@ -1,0 +1,138 @@
+"""The C ABI on the CPU: the library loads, exports what include/gdr.h declares,
+and rejects bad arguments synchronously, before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from gated_delta_rule_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    lib = _lib.load()
+    declared = _declared()
+    assert declared == sorted(_lib.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert lib.gdr_abi_version() == 1
+
+
+def test_status_strings():
+    assert _lib.status_string(0) == "GDR_OK"
+    assert _lib.status_string(-1) == "GDR_ERR_INVALID_ARG"
+    assert _lib.status_string(-2) == "GDR_ERR_UNSUPPORTED"
+    assert _lib.status_string(-3) == "GDR_ERR_HIP"
+    assert _lib.status_string(7) == "GDR_UNKNOWN_STATUS"
+
+
+def _desc(**kw):
+    d = _lib.GdrDesc()
+    d.struct_size = ctypes.sizeof(_lib.GdrDesc)
+    base = dict(batch=1, seq_len=128, num_seqs=1, num_k_heads=16, num_v_heads=48, head_dim_k=128,
+                head_dim_v=128, chunk_size=64, qkv_dtype=1, out_dtype=0, use_qk_l2norm=1, scale=1.0,
+                l2norm_eps=1e-6)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(d, k, v)
+    return d
+
+
+FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
+
+
+def _chunk(d, q=FAKE, cu=None, o=FAKE, init=None, fin=None):
+    lib = _lib.load()
+    return lib.gdr_chunk_fwd(ctypes.byref(d) if d is not None else None, q, FAKE, FAKE, FAKE, FAKE, init, fin,
+                             cu, o, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(num_v_heads=40), -1, "multiple"),
+    (dict(head_dim_k=96, head_dim_v=96), -2, "head dims"),
+    (dict(head_dim_k=128, head_dim_v=64), -2, "head dims"),
+    (dict(chunk_size=48), -2, "chunk_size"),
+    (dict(qkv_dtype=5), -1, "dtype"),
+    (dict(batch=2, num_seqs=3), -1, "num_seqs"),
+    (dict(seq_len=-1), -1, "negative"),
+    (dict(num_k_heads=0), -1, "positive"),
+    (dict(l2norm_eps=-1.0), -1, "eps"),
+    (dict(struct_size=8), -1, "struct_size"),
+])
+def test_chunk_fwd_rejects_bad_descriptors(kw, status, msg):
+    assert _chunk(_desc(**kw)) == status
+    assert msg in _lib.load().gdr_last_error().decode()
+
+
+def test_chunk_fwd_rejects_null_and_misaligned():
+    lib = _lib.load()
+    assert _chunk(None) == -1
+    assert _chunk(_desc(), q=None) == -1 and "required" in lib.gdr_last_error().decode()
+    assert _chunk(_desc(), q=FAKE + 2) == -1 and "aligned" in lib.gdr_last_error().decode()
+    assert _chunk(_desc(), fin=FAKE + 4) == -1
+    assert _chunk(_desc(batch=2, num_seqs=2), cu=FAKE) == -1  # packed batch needs batch == 1
+
+
+def test_workspace_size():
+    lib = _lib.load()
+    n = ctypes.c_size_t(123)
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc()), ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc(batch=1, num_seqs=8)), ctypes.byref(n)) == 0
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc(chunk_size=16)), ctypes.byref(n)) == -2
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc()), None) == -1
+
+
+def test_recurrent_step_validation():
+    lib = _lib.load()
+    d = _desc(batch=4, num_seqs=4, seq_len=1)
+    args = [FAKE] * 5
+    assert lib.gdr_recurrent_step(ctypes.byref(_desc(batch=4, num_seqs=4, seq_len=2)), *args, FAKE, FAKE, None) == -1
+    assert lib.gdr_recurrent_step(ctypes.byref(d), *args, None, FAKE, None) == -1
+    assert lib.gdr_recurrent_step(ctypes.byref(d), *args, FAKE + 8, FAKE, None) == -1
+    assert "aligned" in lib.gdr_last_error().decode()
+
+
+def test_conv_and_norm_validation():
+    lib = _lib.load()
+    c = _lib.GdrConvDesc()
+    c.struct_size = ctypes.sizeof(_lib.GdrConvDesc)
+    c.num_tokens, c.num_seqs, c.num_k_heads, c.num_v_heads, c.head_dim = 16, 1, 16, 48, 128
+    ptrs = [FAKE] * 14
+    assert lib.gdr_conv_gate_fused(ctypes.byref(c), FAKE, FAKE, None, *ptrs[3:], None) == -1  # no cu_seqlens
+    # conv_state_out aliasing conv_state_in
+    assert lib.gdr_conv_gate_fused(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, FAKE, *ptrs[5:], None) == -1
+    assert "alias" in lib.gdr_last_error().decode()
+    c.head_dim = 100
+    assert lib.gdr_conv_gate_fused(ctypes.byref(c), *([FAKE] * 15)) == -2
+    n = _lib.GdrNormDesc()
+    n.struct_size = ctypes.sizeof(_lib.GdrNormDesc)
+    n.num_tokens, n.num_heads, n.head_dim, n.o_dtype, n.eps = 4, 48, 96, 0, 1e-6
+    assert lib.gdr_gated_rmsnorm(ctypes.byref(n), FAKE, FAKE, FAKE, FAKE, None) == -2
+    n.head_dim = 128
+    assert lib.gdr_gated_rmsnorm(ctypes.byref(n), FAKE, FAKE, FAKE, FAKE + 2, None) == -1
+    assert lib.gdr_gated_rmsnorm(None, FAKE, FAKE, FAKE, FAKE, None) == -1
+
+
+def test_no_oracle_in_product_path():
+    """The library and its binding never import the oracle."""
+    pkg = os.path.join(ROOT, "gated_delta_rule_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", src, flags=re.M), f
+                assert "oracle/" not in src and "oracle." not in src, f

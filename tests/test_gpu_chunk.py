@@ -1,0 +1,207 @@
+"""GPU parity of gdr_chunk_fwd (chunked prefill) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+from gated_delta_rule_amd import synth
+from oracle import gdr as ref
+from helpers import BF16_TOL, F32_TOL, bits_equal, gpu, rel_err, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_inputs(x, dev, cu=None, s0=None):
+    return dict(q=to_dev(x.q, x.dtype, dev), k=to_dev(x.k, x.dtype, dev), v=to_dev(x.v, x.dtype, dev),
+                g=to_dev(x.g, "f32", dev), beta=to_dev(x.beta, "f32", dev),
+                initial_state=None if s0 is None else to_dev(s0, "f32", dev),
+                cu_seqlens=None if cu is None else to_dev(cu, "i32", dev))
+
+
+def _gpu_chunk(x, cu=None, s0=None, **kw):
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    a = _dev_inputs(x, dev, cu, s0)
+    o, s = gdr_amd.chunk_gated_delta_rule(a["q"], a["k"], a["v"], a["g"], a["beta"], a["initial_state"],
+                                          output_final_state=True, cu_seqlens=a["cu_seqlens"],
+                                          chunk_size=x.chunk_size, **kw)
+    torch.cuda.synchronize()
+    return o, s
+
+
+def _check(x, cu=None, s0=None, tol=BF16_TOL, heads=None, procs=None, **kw):
+    o, s = _gpu_chunk(x, cu, s0, **kw)
+    o_ref, s_ref, _ = ref.forward_parallel(x.q, x.k, x.v, x.g, x.beta, s0, cu, processes=procs)
+    og, sg = to_host(o), to_host(s)
+    eo, es = rel_err(og, o_ref), rel_err(sg, s_ref)
+    say(f"  o err {eo:.2e}  state err {es:.2e}  (tol {tol:g})")
+    assert np.isfinite(og).all() and np.isfinite(sg).all()
+    assert eo <= tol and es <= tol
+    return o, s
+
+
+def test_tiny_fp32_config():
+    """B=1, T=128, 2/6 heads, d=32, chunk 32, all fp32 (the small oracle config)."""
+    say("chunk tiny fp32 d=32 C=32")
+    _check(synth.tiny_config(), tol=F32_TOL)
+
+
+def test_layer_prefill_4096():
+    """B=1, T=4096, 16/48 heads, d=128, bf16 q/k/v, chunk 64, zero state."""
+    say("chunk layer prefill T=4096 bf16")
+    _check(synth.layer_prefill(T=4096))
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+def test_ragged_lengths_with_initial_state(T):
+    x = synth.gdr_inputs(10 + T, B=2, T=T, hk=16, hv=48, d=128, dtype="bf16", initial_state_std=0.05)
+    say(f"chunk bf16 B=2 T={T} with initial state")
+    _check(x, s0=x.initial_state)
+
+
+def test_varlen_packed_with_empty_and_short_sequences():
+    lens = [0, 1, 130, 64, 3, 0, 257, 5]
+    cu = synth.cu_seqlens_of(lens)
+    x = synth.gdr_inputs(21, B=1, T=int(cu[-1]), dtype="bf16")
+    s0 = (0.05 * np.random.default_rng(22).standard_normal((len(lens), 48, 128, 128))).astype(np.float32)
+    say(f"chunk varlen {lens}")
+    _check(x, cu=cu, s0=s0)
+
+
+def test_varlen_packed_equals_separate_bit_exact():
+    import torch
+    lens = [70, 1, 129, 64]
+    cu = synth.cu_seqlens_of(lens)
+    x = synth.gdr_inputs(23, B=1, T=int(cu[-1]), dtype="bf16")
+    s0 = (0.05 * np.random.default_rng(24).standard_normal((len(lens), 48, 128, 128))).astype(np.float32)
+    say("chunk varlen packed vs separate (bit-exact)")
+    o, s = _gpu_chunk(x, cu=cu, s0=s0)
+    for n in range(len(lens)):
+        sl = slice(cu[n], cu[n + 1])
+        xn = synth.GDRInputs(x.q[:, sl], x.k[:, sl], x.v[:, sl], x.g[:, sl], x.beta[:, sl], x.A_log,
+                             x.dt_bias, "bf16", 64)
+        on, sn = _gpu_chunk(xn, s0=s0[n:n + 1])
+        assert bits_equal(o[:, cu[n]:cu[n + 1]], on)
+        assert bits_equal(s[n:n + 1], sn)
+
+
+def test_nan_in_one_sequence_stays_there():
+    import torch
+    lens = [100, 90, 80]
+    cu = synth.cu_seqlens_of(lens)
+    x = synth.gdr_inputs(25, B=1, T=int(cu[-1]), dtype="bf16")
+    say("chunk NaN isolation")
+    o1, s1 = _gpu_chunk(x, cu=cu)
+    v = x.v.copy()
+    v[0, cu[1] + 7] = np.nan
+    x2 = synth.GDRInputs(x.q, x.k, v, x.g, x.beta, x.A_log, x.dt_bias, "bf16", 64)
+    o2, s2 = _gpu_chunk(x2, cu=cu)
+    for n in (0, 2):
+        assert bits_equal(o1[:, cu[n]:cu[n + 1]], o2[:, cu[n]:cu[n + 1]])
+        assert bits_equal(s1[n], s2[n])
+    assert torch.isnan(s2[1]).any()
+
+
+def test_chained_calls_equal_single_call_bit_exact():
+    """Resume at chunk multiples: 4 x 256 chained calls == one 1024-token call."""
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    x = synth.gdr_inputs(26, B=1, T=1024, dtype="bf16")
+    say("chunk chained 4x256 vs single 1024")
+    o, s = _gpu_chunk(x)
+    a = _dev_inputs(x, dev)
+    state = torch.zeros((1, 48, 128, 128), device=dev)
+    outs = []
+    for i in range(4):
+        sl = slice(256 * i, 256 * (i + 1))
+        oi, _ = gdr_amd.chunk_gated_delta_rule(a["q"][:, sl].contiguous(), a["k"][:, sl].contiguous(),
+                                               a["v"][:, sl].contiguous(), a["g"][:, sl].contiguous(),
+                                               a["beta"][:, sl].contiguous(), state, final_state=state)
+        outs.append(oi)
+    torch.cuda.synchronize()
+    assert bits_equal(torch.cat(outs, 1), o)
+    assert bits_equal(state, s)
+
+
+def test_deterministic():
+    x = synth.layer_prefill(T=700)
+    say("chunk determinism T=700")
+    o1, s1 = _gpu_chunk(x)
+    o2, s2 = _gpu_chunk(x)
+    assert bits_equal(o1, o2) and bits_equal(s1, s2)
+
+
+@pytest.mark.parametrize("d,dtype,C", [(64, "bf16", 64), (64, "f32", 64), (128, "f32", 64), (128, "bf16", 32),
+                                       (32, "bf16", 32)])
+def test_other_shapes_fp32_path(d, dtype, C):
+    x = synth.gdr_inputs(30 + d + C, B=1, T=150, hk=2, hv=6, d=d, dtype=dtype, chunk_size=C,
+                         initial_state_std=0.05)
+    say(f"chunk fp32 path d={d} {dtype} C={C}")
+    _check(x, s0=x.initial_state, tol=F32_TOL if dtype == "f32" else BF16_TOL)
+
+
+def test_bf16_output():
+    import torch
+    x = synth.layer_prefill(T=300)
+    say("chunk bf16 output T=300")
+    o, s = _gpu_chunk(x, out_dtype=torch.bfloat16)
+    o_ref, s_ref, _ = ref.forward_parallel(x.q, x.k, x.v, x.g, x.beta)
+    og = to_host(o)
+    rms = np.sqrt(np.mean(o_ref ** 2))
+    from helpers import bf16_ulp
+    assert np.all(np.abs(og - o_ref) <= bf16_ulp(o_ref) + BF16_TOL * rms)
+    assert rel_err(to_host(s), s_ref) <= BF16_TOL
+
+
+def test_query_scale_and_no_l2norm():
+    x = synth.gdr_inputs(40, B=1, T=130, dtype="bf16")
+    say("chunk scale=0.088, use_qk_l2norm=False")
+    o, s = _gpu_chunk(x, scale=0.088, use_qk_l2norm_in_kernel=False)
+    o_ref, s_ref, _ = ref.forward_parallel(x.q, x.k, x.v, x.g, x.beta, use_qk_l2norm=False, scale=0.088)
+    assert rel_err(to_host(o), o_ref) <= BF16_TOL and rel_err(to_host(s), s_ref) <= BF16_TOL
+
+
+def test_long_context_resume():
+    """T = 262144 as 8 chained 32768-token calls (final_state -> initial_state).
+
+    Oracle: the first 4096 outputs of call 0, and the final state after a
+    16384-token prefix, which the GPU computes both as one call and as 4
+    chained 4096-token calls (these two must also agree bit for bit).
+    """
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    x0 = synth.long_context_call(0)
+    say("long context: call 0 prefix checks")
+    a = _dev_inputs(x0, dev)
+    o_full, _ = gdr_amd.chunk_gated_delta_rule(a["q"], a["k"], a["v"], a["g"], a["beta"])
+    o_ref, _, _ = ref.forward_parallel(x0.q[:, :4096], x0.k[:, :4096], x0.v[:, :4096], x0.g[:, :4096],
+                                       x0.beta[:, :4096])
+    torch.cuda.synchronize()
+    assert rel_err(to_host(o_full[:, :4096]), o_ref) <= BF16_TOL
+    P = 16384
+    sl = lambda t, i, j: t[:, i:j].contiguous()
+    _, s_one = gdr_amd.chunk_gated_delta_rule(sl(a["q"], 0, P), sl(a["k"], 0, P), sl(a["v"], 0, P),
+                                              sl(a["g"], 0, P), sl(a["beta"], 0, P), output_final_state=True)
+    st = torch.zeros((1, 48, 128, 128), device=dev)
+    for i in range(4):
+        j0, j1 = 4096 * i, 4096 * (i + 1)
+        gdr_amd.chunk_gated_delta_rule(sl(a["q"], j0, j1), sl(a["k"], j0, j1), sl(a["v"], j0, j1),
+                                       sl(a["g"], j0, j1), sl(a["beta"], j0, j1), st, final_state=st)
+    torch.cuda.synchronize()
+    assert bits_equal(s_one, st)
+    _, s_ref, _ = ref.forward_parallel(x0.q[:, :P], x0.k[:, :P], x0.v[:, :P], x0.g[:, :P], x0.beta[:, :P])
+    assert rel_err(to_host(s_one), s_ref) <= BF16_TOL
+    say("long context: 8 chained 32K calls")
+    state = torch.zeros((1, 48, 128, 128), device=dev)
+    norms = []
+    for i in range(8):
+        xi = x0 if i == 0 else synth.long_context_call(i)
+        ai = a if i == 0 else _dev_inputs(xi, dev)
+        o, _ = gdr_amd.chunk_gated_delta_rule(ai["q"], ai["k"], ai["v"], ai["g"], ai["beta"], state,
+                                              final_state=state)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all() and torch.isfinite(state).all()
+        norms.append(float(state.norm()))
+    # beta <= 1 and unit keys bound every state row by max |v| / (1 - max alpha); no blow-up
+    assert max(norms) < 1e3

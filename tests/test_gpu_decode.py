@@ -1,0 +1,100 @@
+"""GPU parity of gdr_recurrent_step (one-token decode) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+from gated_delta_rule_amd import synth
+from oracle import gdr as ref
+from helpers import BF16_TOL, F32_TOL, bits_equal, gpu, rel_err, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_steps(N, hk, hv, d, dtype, steps, seqs_checked=None, out_dtype="f32"):
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    A_log, dt, s0 = synth.decode_inputs(N=N, hk=hk, hv=hv, d=d)
+    state = to_dev(s0, "f32", dev)
+    sel = np.arange(N) if seqs_checked is None else np.asarray(seqs_checked)
+    S_ref = s0[sel].astype(np.float64)
+    worst_o = 0.0
+    odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    for step in range(steps):
+        x = synth.decode_step_inputs(step, N=N, hk=hk, hv=hv, d=d, dtype=dtype)
+        o = gdr_amd.recurrent_step(to_dev(x.q, dtype, dev), to_dev(x.k, dtype, dev), to_dev(x.v, dtype, dev),
+                                   to_dev(x.g, "f32", dev), to_dev(x.beta, "f32", dev), state, out_dtype=odt)
+        o_ref, S_ref = ref.decode_step(x.q[sel], x.k[sel], x.v[sel], x.g[sel], x.beta[sel], S_ref)
+        worst_o = max(worst_o, rel_err(to_host(o)[sel], o_ref))
+    torch.cuda.synchronize()
+    return worst_o, rel_err(to_host(state)[sel], S_ref)
+
+
+def test_decode_layer_shape_8_steps():
+    say("decode N=64 Hk=16 Hv=48 d=128 bf16, 8 steps")
+    eo, es = _run_steps(64, 16, 48, 128, "bf16", 8)
+    say(f"  o err {eo:.2e}  state err {es:.2e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
+
+
+def test_decode_layer_shape_256_steps_sampled():
+    """All 64 sequences run 256 in-place steps on the GPU; the oracle follows two of them."""
+    say("decode N=64 bf16, 256 steps, oracle on sequences 5 and 62")
+    eo, es = _run_steps(64, 16, 48, 128, "bf16", 256, seqs_checked=[5, 62])
+    say(f"  o err {eo:.2e}  state err {es:.2e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_decode_fp32(d):
+    say(f"decode fp32 N=5 Hk=2 Hv=6 d={d}")
+    eo, es = _run_steps(5, 2, 6, d, "f32", 6)
+    say(f"  o err {eo:.2e}  state err {es:.2e}")
+    assert eo <= F32_TOL and es <= F32_TOL
+
+
+def test_decode_bf16_output():
+    say("decode bf16 out N=8")
+    eo, es = _run_steps(8, 16, 48, 128, "bf16", 3, out_dtype="bf16")
+    # bf16 storage of o adds up to half a bf16 ulp of the largest output
+    assert eo <= 2e-2 and es <= BF16_TOL
+
+
+def test_decode_matches_one_token_prefill():
+    """Cross-kernel layout check: decode step = chunked prefill with T = 1."""
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    say("decode vs chunk_fwd T=1, N=4")
+    A_log, dt, s0 = synth.decode_inputs(N=4)
+    x = synth.decode_step_inputs(0, N=4)
+    st1 = to_dev(s0, "f32", dev)
+    o1 = gdr_amd.recurrent_step(to_dev(x.q, "bf16", dev), to_dev(x.k, "bf16", dev), to_dev(x.v, "bf16", dev),
+                                to_dev(x.g, "f32", dev), to_dev(x.beta, "f32", dev), st1)
+    o2, st2 = gdr_amd.chunk_gated_delta_rule(
+        to_dev(x.q[:, None], "bf16", dev), to_dev(x.k[:, None], "bf16", dev), to_dev(x.v[:, None], "bf16", dev),
+        to_dev(x.g[:, None], "f32", dev), to_dev(x.beta[:, None], "f32", dev), to_dev(s0, "f32", dev),
+        output_final_state=True)
+    torch.cuda.synchronize()
+    assert rel_err(to_host(o2)[:, 0], to_host(o1)) <= BF16_TOL
+    assert rel_err(to_host(st2), to_host(st1)) <= BF16_TOL
+
+
+def test_decode_deterministic_and_empty_batch():
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    say("decode determinism N=16")
+    A_log, dt, s0 = synth.decode_inputs(N=16)
+    x = synth.decode_step_inputs(1, N=16)
+    args = [to_dev(x.q, "bf16", dev), to_dev(x.k, "bf16", dev), to_dev(x.v, "bf16", dev),
+            to_dev(x.g, "f32", dev), to_dev(x.beta, "f32", dev)]
+    sa, sb = to_dev(s0, "f32", dev), to_dev(s0, "f32", dev)
+    oa = gdr_amd.recurrent_step(*args, sa)
+    ob = gdr_amd.recurrent_step(*args, sb)
+    torch.cuda.synchronize()
+    assert bits_equal(oa, ob) and bits_equal(sa, sb)
+    e = torch.empty((0, 16, 128), device=dev, dtype=torch.bfloat16)
+    ev = torch.empty((0, 48, 128), device=dev, dtype=torch.bfloat16)
+    ef = torch.empty((0, 48), device=dev)
+    es = torch.empty((0, 48, 128, 128), device=dev)
+    assert gdr_amd.recurrent_step(e, e, ev, ef, ef, es).shape == (0, 48, 128)
