@@ -9,24 +9,35 @@ from helpers import BF16_TOL, F32_TOL, bits_equal, gpu, rel_err, say, to_dev, to
 pytestmark = pytest.mark.gpu
 
 
-def _run_steps(N, hk, hv, d, dtype, steps, seqs_checked=None, out_dtype="f32"):
+def _run_steps(N, hk, hv, d, dtype, steps, seqs_checked=None, out_dtype="f32", elementwise=False):
+    """Run ``steps`` in-place decode steps on the GPU beside the oracle.
+
+    Returns the worst output error, the final state error (both max|gpu-ref|/RMS),
+    and, if ``elementwise``, the worst ratio |gpu-ref| / (bf16 ulp(ref) + tol*RMS).
+    """
     import gated_delta_rule_amd as gdr_amd
     import torch
+    from helpers import bf16_ulp
     dev = gpu()
     A_log, dt, s0 = synth.decode_inputs(N=N, hk=hk, hv=hv, d=d)
     state = to_dev(s0, "f32", dev)
     sel = np.arange(N) if seqs_checked is None else np.asarray(seqs_checked)
     S_ref = s0[sel].astype(np.float64)
-    worst_o = 0.0
+    worst_o, worst_ratio = 0.0, 0.0
     odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
     for step in range(steps):
         x = synth.decode_step_inputs(step, N=N, hk=hk, hv=hv, d=d, dtype=dtype)
         o = gdr_amd.recurrent_step(to_dev(x.q, dtype, dev), to_dev(x.k, dtype, dev), to_dev(x.v, dtype, dev),
                                    to_dev(x.g, "f32", dev), to_dev(x.beta, "f32", dev), state, out_dtype=odt)
         o_ref, S_ref = ref.decode_step(x.q[sel], x.k[sel], x.v[sel], x.g[sel], x.beta[sel], S_ref)
-        worst_o = max(worst_o, rel_err(to_host(o)[sel], o_ref))
+        og = to_host(o)[sel]
+        worst_o = max(worst_o, rel_err(og, o_ref))
+        if elementwise:
+            bound = bf16_ulp(o_ref) + BF16_TOL * np.sqrt(np.mean(o_ref ** 2))
+            worst_ratio = max(worst_ratio, float(np.max(np.abs(og - o_ref) / bound)))
     torch.cuda.synchronize()
-    return worst_o, rel_err(to_host(state)[sel], S_ref)
+    es = rel_err(to_host(state)[sel], S_ref)
+    return (worst_o, es, worst_ratio) if elementwise else (worst_o, es)
 
 
 def test_decode_layer_shape_8_steps():
@@ -53,10 +64,12 @@ def test_decode_fp32(d):
 
 
 def test_decode_bf16_output():
+    """bf16 storage of o: each output within one bf16 ulp of the oracle, plus the
+    fp32-path tolerance; the state (always fp32) within the usual tolerance."""
     say("decode bf16 out N=8")
-    eo, es = _run_steps(8, 16, 48, 128, "bf16", 3, out_dtype="bf16")
-    # bf16 storage of o adds up to half a bf16 ulp of the largest output
-    assert eo <= 2e-2 and es <= BF16_TOL
+    eo, es, ratio = _run_steps(8, 16, 48, 128, "bf16", 3, out_dtype="bf16", elementwise=True)
+    say(f"  worst |o - ref| / (ulp + tol*rms) = {ratio:.3f}, state err {es:.2e}")
+    assert ratio <= 1.0 and es <= BF16_TOL
 
 
 def test_decode_matches_one_token_prefill():
