@@ -97,12 +97,31 @@ const char* gdr_status_string(int status) {
 
 const char* gdr_last_error(void) { return g_last_error.c_str(); }
 
+// The MFMA path (bf16 q/k/v, d = 128, chunk 64) keeps per-chunk records in a
+// workspace; every other combination needs none.
+static bool mfma_path(const gdr_desc* d) {
+  return d->qkv_dtype == GDR_BF16 && d->head_dim_k == 128 && d->chunk_size == 64;
+}
+
+static size_t workspace_bytes_for(const gdr_desc* d) {
+  if (!mfma_path(d)) return 0;
+  gdr::ChunkArgs a{};
+  a.N = d->num_seqs;
+  a.T = d->seq_len;
+  a.Hv = d->num_v_heads;
+  // With batch == 1 the same descriptor may describe a packed batch, whose
+  // chunk count is bounded by ceil(T/64) + N; size for that bound.
+  static const int32_t any_cu = 0;
+  a.cu_seqlens = d->batch == 1 ? &any_cu : nullptr;
+  return gdr::chunk_bf16_workspace_bytes(a);
+}
+
 gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* d, size_t* bytes) {
   if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
   // a packed batch (cu_seqlens) is the only way num_seqs can differ from batch
   gdr_status st = check_desc(d, false, d && d->num_seqs != d->batch);
   if (st != GDR_OK) return st;
-  *bytes = 0;
+  *bytes = workspace_bytes_for(d);
   return ok();
 }
 
@@ -110,8 +129,6 @@ gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const 
                          const float* beta, const float* initial_state, float* final_state,
                          const int32_t* cu_seqlens, void* o, void* workspace, size_t workspace_bytes,
                          void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   gdr_status st = check_desc(d, false, cu_seqlens != nullptr);
   if (st != GDR_OK) return st;
   const long long tokens = (long long)d->batch * d->seq_len;
@@ -122,6 +139,10 @@ gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const 
       !aligned16(final_state))
     return fail(GDR_ERR_INVALID_ARG, "q, k, v, o and state pointers must be 16-byte aligned");
   if (d->num_seqs == 0) return ok();
+  const size_t need = workspace_bytes_for(d);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(GDR_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace ? workspace_bytes : 0);
+  if (need > 0 && !aligned16(workspace)) return fail(GDR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   gdr::ChunkArgs a{};
   a.q = q;
   a.k = k;
@@ -144,8 +165,8 @@ gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const 
   a.scale = d->scale;
   a.eps = d->l2norm_eps;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool mfma = a.qkv_bf16 && a.D == 128 && a.C == 64;
-  return hip_status(mfma ? gdr::launch_chunk_bf16(a, s) : gdr::launch_chunk_f32(a, s), "gdr_chunk_fwd launch");
+  return hip_status(mfma_path(d) ? gdr::launch_chunk_bf16(a, workspace, s) : gdr::launch_chunk_f32(a, s),
+                    "gdr_chunk_fwd launch");
 }
 
 gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,

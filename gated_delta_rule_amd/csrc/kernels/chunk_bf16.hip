@@ -12,17 +12,19 @@
 //   O     = scale diag(e^G) Q^ S0^T + P Delta,  P_ij = scale Gamma_ij q^_i . k^_j (j <= i)
 //   S_L   = e^{G_L} S0 + (diag(Gamma_{L,:}) Delta)^T K^
 //
-// Work split: one workgroup of 4 waves per (sequence, value head, 64 value
-// channels); wave w owns 16 value channels of the state for the whole
-// sequence and runs their chain (X = K S0^T, R, Delta, O, S update) without
-// exchanging data with other waves.  The matrix-core output layout (lane l
-// holds rows 4*(l/16)+i of column l%16) is fed back as the B operand of the
-// next contraction by permuting the contraction index identically on both
-// operands, so R, Delta and the state stay in registers.  The shared A
-// operands (K, Q, K^T, T, P) live in LDS with their contraction index stored
-// in that permuted order, so each fragment is one 16-byte read.  The chunk's
-// setup (Gram matrices, norms, decays, T) is shared by the 4 waves; the next
-// chunk's global loads are issued before the state phase of the current one.
+// Two kernels.  The part that does not depend on the state -- Gram matrices,
+// q/k norms, decays, T and P -- is computed by chunk_prep_kernel, one
+// workgroup per (chunk, value head), all chunks of all sequences in parallel,
+// into a caller-provided workspace.  chunk_rec_kernel then carries the state:
+// one workgroup of 4 waves per (sequence, value head, 64 value channels),
+// wave w owning 16 value channels for the whole sequence, chunk after chunk:
+// X = K S0^T, R, Delta = T R, O, S update.  The matrix-core output layout
+// (lane l holds rows 4*(l/16)+i of column l%16) is fed back as the B operand
+// of the next contraction by permuting the contraction index identically on
+// both operands, so R, Delta and the state stay in registers; the shared A
+// operands (K, Q, K^T, T, P) sit in LDS with their contraction index stored in
+// that permuted order, so each fragment is one 16-byte read.  The next
+// chunk's inputs are loaded while the current chunk's state phase runs.
 //
 // Precision: q, k, v are exact bf16 MFMA operands; L2-norm factors and gates
 // are fp32 scales applied after the products.  Every computed operand (state,
@@ -39,9 +41,17 @@ namespace {
 
 constexpr int kD = 128;  // head dim (d_k = d_v)
 constexpr int kC = 64;   // chunk
-constexpr int kNW = 4;   // waves per workgroup
-constexpr int kNT = 64 * kNW;
-constexpr int kDVS = 16 * kNW;  // value channels per workgroup
+constexpr int kNT = 256;  // threads per workgroup (4 waves)
+constexpr int kDVS = 64;  // value channels per recurrence workgroup
+
+// Workspace record of one (chunk, value head), in bytes: T hi, T lo, P hi,
+// P lo (each: rows 0..31 x 32 columns, then rows 32..63 x 64 columns, bf16,
+// columns permuted), then token factors bt, xr, yq, cL (fp32 x 64 each) and
+// e^{G_L}.
+constexpr int kMatBytes = 6144;
+constexpr int kFacOff = 4 * kMatBytes;
+constexpr size_t kRecBytes = 25728;
+constexpr size_t kTableBytes(int N) { return (((size_t)N + 1) * 4 + 255) / 256 * 256; }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -59,23 +69,8 @@ __device__ __forceinline__ int perm32(int x) {
 __device__ __forceinline__ int perm8(int b) {
   return 32 * (b >> 2) + ((0x14041000u >> (8 * (b & 3))) & 0xff);
 }
-
-struct __align__(16) Smem {
-  uint16_t Kr[kC][kD + 8];   // k rows, columns permuted
-  uint16_t Qr[kC][kD + 8];   // q rows, columns permuted
-  uint16_t Kt[kD][kC + 8];   // k transposed, tokens permuted
-  uint16_t Th[kC][kC + 8], Tl[kC][kC + 8];  // T hi/lo, columns permuted
-  uint16_t Ph[kC][kC + 8], Pl[kC][kC + 8];  // P hi/lo, columns permuted
-  float A[kC][kC + 4];
-  float Tf[kC][kC + 4];
-  float Ys[32][36];
-  float ssk[kC], ssq[kC];            // squared norms
-  float G2[kC];                      // cumulative log2-decay
-  float rk[kC], ar[kC], pr[kC];      // column / row factors of A and P
-  float bt[kC], xr[kC], yq[kC], cL[kC];  // token factors of the state phase
-  float gin[kC], bin[kC];
-  float eGL;
-};
+// Element offset of (row i, physical column p) in a compact T/P matrix.
+__device__ __forceinline__ int compact_idx(int i, int p) { return i < 32 ? i * 32 + p : 1024 + (i - 32) * 64 + p; }
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
@@ -140,61 +135,456 @@ __device__ __forceinline__ f32x4 tile_mm_f32(const float* m1, int ld1, const flo
   return mfma3(ah, al, bh, bl, f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
-// Registers holding one chunk's global inputs between issue and LDS store.
-struct ChunkRegs {
-  u16x8 kq[8];      // 8 rows x 8 columns of k (threads 0..127) or q (128..255)
-  uint16_t vv[16];  // this lane's v values in accumulator layout
-  float gb;         // g (wave 0) or beta (wave 1) of token `lane`
+// Sequence of chunk j and its token range [c0, c0 + L).
+struct ChunkPos {
+  int n, c0, L;
+  bool valid;
 };
 
-template <bool kFull>
-__device__ __forceinline__ void issue_loads(ChunkRegs& r, const ChunkArgs& a, int c0, int L, int kh, int h,
-                                            int vcol, int tid, int lane, int wave, int q4) {
-  const uint16_t* src = static_cast<const uint16_t*>(tid < 128 ? a.k : a.q);
-  const int b = tid & 127, rb = b >> 4, cb = b & 15;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 8 * rb + i;
-    if (kFull || row < L)
-      r.kq[i] = *reinterpret_cast<const u16x8*>(src + ((size_t)(c0 + row) * a.Hk + kh) * kD + 8 * cb);
-    else
-      r.kq[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-  }
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v);
-#pragma unroll
-  for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int t = 16 * ti + 4 * q4 + i4;
-      r.vv[4 * ti + i4] = (kFull || t < L) ? vg[((size_t)(c0 + t) * a.Hv + h) * kD + vcol] : uint16_t(0);
+__device__ __forceinline__ ChunkPos locate_chunk(const ChunkArgs& a, const int32_t* table, int j) {
+  ChunkPos p;
+  if (a.cu_seqlens) {
+    if (j >= table[a.N]) { p.valid = false; return p; }
+    int lo = 0, hi = a.N;  // table[lo] <= j < table[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (table[mid] <= j) lo = mid; else hi = mid;
     }
-  r.gb = 0.f;
+    p.n = lo;
+    p.c0 = a.cu_seqlens[lo] + (j - table[lo]) * kC;
+    p.L = min(kC, a.cu_seqlens[lo + 1] - p.c0);
+  } else {
+    const int per = (a.T + kC - 1) / kC;
+    p.n = j / per;
+    const int i = j - p.n * per;
+    p.c0 = p.n * a.T + i * kC;
+    p.L = min(kC, a.T - i * kC);
+  }
+  p.valid = true;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Chunk table: table[n] = number of chunks of sequences 0..n-1.
+
+__global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, int N, int32_t* table) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (N + 1023) / 1024;
+  const int n0 = min(N, t * per), n1 = min(N, n0 + per);
+  int sum = 0;
+  for (int n = n0; n < n1; ++n) sum += (cu[n + 1] - cu[n] + kC - 1) / kC;
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = t ? part[t - 1] : 0;
+  for (int n = n0; n < n1; ++n) {
+    table[n] = run;
+    run += (cu[n + 1] - cu[n] + kC - 1) / kC;
+  }
+  if (t == 1023) table[N] = part[1023];
+}
+
+// ---------------------------------------------------------------------------
+// Chunk preparation: T = (I + A)^{-1}, P and token factors of one
+// (chunk, value head).
+
+struct __align__(16) PrepSmem {
+  uint16_t Kr[kC][kD + 8];   // k rows, columns permuted
+  uint16_t Qr[kC][kD + 8];   // q rows, columns permuted
+  float A[kC][kC + 4];
+  float Tf[kC][kC + 4];
+  float Ys[32][36];
+  float ssk[kC], ssq[kC];
+  float G2[kC], rk[kC], ar[kC], pr[kC];
+  float gin[kC], bin[kC];
+};
+
+__global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigned char* ws) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int c = lane & 15, q4 = lane >> 4;
+  const int j = blockIdx.x, h = blockIdx.y;
+  const int32_t* table = reinterpret_cast<const int32_t*>(ws);
+  const ChunkPos pos = locate_chunk(a, table, j);
+  if (!pos.valid) return;
+  const int c0 = pos.c0, L = pos.L;
+  const int kh = h / (a.Hv / a.Hk);
+  unsigned char* rec = ws + kTableBytes(a.N) + ((size_t)j * a.Hv + h) * kRecBytes;
+  uint16_t* Thg = reinterpret_cast<uint16_t*>(rec);
+  uint16_t* Tlg = reinterpret_cast<uint16_t*>(rec + kMatBytes);
+  uint16_t* Phg = reinterpret_cast<uint16_t*>(rec + 2 * kMatBytes);
+  uint16_t* Plg = reinterpret_cast<uint16_t*>(rec + 3 * kMatBytes);
+  float* facg = reinterpret_cast<float*>(rec + kFacOff);
+
+  // ---- k, q rows to LDS with permuted columns; g, beta
+  {
+    const uint16_t* src = static_cast<const uint16_t*>(tid < 128 ? a.k : a.q);
+    uint16_t(*X)[kD + 8] = tid < 128 ? sm.Kr : sm.Qr;
+    const int b = tid & 127, rb = b >> 4, cb = b & 15;
+    const int pc = perm8(cb);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = 8 * rb + i;
+      u16x8 val = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (row < L) val = *reinterpret_cast<const u16x8*>(src + ((size_t)(c0 + row) * a.Hk + kh) * kD + 8 * cb);
+      const u32x4 w = __builtin_bit_cast(u32x4, val);
+      *reinterpret_cast<u32x2*>(&X[row][pc]) = u32x2{w[0], w[1]};
+      *reinterpret_cast<u32x2*>(&X[row][pc + 8]) = u32x2{w[2], w[3]};
+    }
+    if (wave < 2) {
+      const float* p = wave == 0 ? a.g : a.beta;
+      (wave == 0 ? sm.gin : sm.bin)[lane] = lane < L ? p[(size_t)(c0 + lane) * a.Hv + h] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- Gram tiles (raw bf16 products): job 0..9 K_j K_i^T, 10..19 K_j Q_i^T,
+  // 20..23 Q_i Q_i^T (diagonal only, for the q norms).  Lane holds
+  // G[row i = 16 ti + c][cols j = 16 tj + 4 q4 .. +3].
+  f32x4 gacc[5];
+  int gti[5], gtj[5];
+#pragma unroll
+  for (int u = 0; u < 6; ++u) {
+    const int job = wave + 4 * u;
+    int ti, tj;
+    const uint16_t(*XA)[kD + 8];
+    const uint16_t(*XB)[kD + 8];
+    if (job < 20) {
+      const int idx = job % 10;
+      ti = idx >= 6 ? 3 : (idx >= 3 ? 2 : (idx >= 1 ? 1 : 0));
+      tj = idx - ti * (ti + 1) / 2;
+      XA = sm.Kr;
+      XB = job < 10 ? sm.Kr : sm.Qr;
+    } else {
+      ti = tj = job - 20;
+      XA = sm.Qr;
+      XB = sm.Qr;
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma16x16x32(lds8(&XA[16 * tj + c][32 * ks + 8 * q4]), lds8(&XB[16 * ti + c][32 * ks + 8 * q4]), acc);
+    if (u < 5) {
+      gacc[u] = acc;
+      gti[u] = ti;
+      gtj[u] = tj;
+    }
+    if (ti == tj && (job < 10 || job >= 20) && (c >> 2) == q4) (job < 10 ? sm.ssk : sm.ssq)[16 * ti + c] = acc[c & 3];
+  }
+  __syncthreads();
+
+  // ---- per-token factors (wave 0): norms, fp64 cumulative decay, scales
+  if (wave == 0) {
+    const float rkv = a.use_l2 ? 1.f / sqrtf(sm.ssk[lane] + a.eps) : 1.f;
+    const float rqv = a.use_l2 ? 1.f / sqrtf(sm.ssq[lane] + a.eps) : 1.f;
+    double G = (double)sm.gin[lane];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double o = __shfl_up(G, off, 64);
+      if (lane >= off) G += o;
+    }
+    const float g2 = (float)(G * 1.4426950408889634);
+    const float g2L = __shfl(g2, 63, 64);
+    const float eG = exp2f(g2);
+    const float bv = sm.bin[lane];
+    sm.G2[lane] = g2;
+    sm.rk[lane] = rkv;
+    sm.ar[lane] = bv * rkv;
+    sm.pr[lane] = a.scale * rqv;
+    facg[lane] = bv;                         // bt
+    facg[64 + lane] = bv * eG * rkv;         // xr
+    facg[128 + lane] = a.scale * rqv * eG;   // yq
+    facg[192 + lane] = rkv * exp2f(g2L - g2);  // cL
+    if (lane == 0) facg[256] = exp2f(g2L);   // e^{G_L}
+  }
+  __syncthreads();
+
+  // ---- scale Gram tiles into A (fp32, LDS) and P (hi/lo bf16, workspace)
+#pragma unroll
+  for (int u = 0; u < 5; ++u) {
+    const int job = wave + 4 * u;
+    if (job >= 20) break;
+    const int ti = gti[u], tj = gtj[u];
+    const int i = 16 * ti + c, j0 = 16 * tj + 4 * q4;
+    const float g2i = sm.G2[i];
+    const f32x4 g2j = *reinterpret_cast<const f32x4*>(&sm.G2[j0]);
+    const f32x4 rkj = *reinterpret_cast<const f32x4*>(&sm.rk[j0]);
+    const float rowf = job < 10 ? sm.ar[i] : sm.pr[i];
+    f32x4 val;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jj = j0 + e;
+      const bool keep = job < 10 ? (jj < i) : (jj <= i);
+      val[e] = keep ? rowf * rkj[e] * exp2f(g2i - g2j[e]) * gacc[u][e] : 0.f;
+    }
+    if (job < 10) {
+      *reinterpret_cast<f32x4*>(&sm.A[i][j0]) = val;
+    } else {
+      u32x2 hi, lo;
+      split4(val, hi, lo);
+      const int off = compact_idx(i, perm32(j0));
+      *reinterpret_cast<u32x2*>(Phg + off) = hi;
+      *reinterpret_cast<u32x2*>(Plg + off) = lo;
+    }
+  }
+  // zero the above-diagonal tiles (0,1) and (2,3) that 32-wide steps read
   if (wave < 2) {
-    const float* p = wave == 0 ? a.g : a.beta;
-    r.gb = (kFull || lane < L) ? p[(size_t)(c0 + lane) * a.Hv + h] : 0.f;
+    const int i = 32 * wave + c;
+    const int off = compact_idx(i, perm32(32 * wave + 16 + 4 * q4));
+    *reinterpret_cast<u32x2*>(Phg + off) = u32x2{0u, 0u};
+    *reinterpret_cast<u32x2*>(Plg + off) = u32x2{0u, 0u};
+    *reinterpret_cast<f32x4*>(&sm.Tf[i][32 * wave + 16 + 4 * q4]) = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+
+  // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution
+  // (wave w inverts block w; lane c < 16 computes column c)
+  if (lane < 16) {
+    const int b = wave;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      const float* arow = &sm.A[16 * b + r][16 * b];
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int m4 = 0; m4 < r; m4 += 4) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(arow + m4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (m4 + e < r) {
+            if (e & 1) s1 += av[e] * x[m4 + e];
+            else s0 += av[e] * x[m4 + e];
+          }
+      }
+      x[r] = (r > c) ? -(s0 + s1) : x[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm.Tf[16 * b + r][16 * b + c] = x[r];
+  }
+  __syncthreads();
+  // level 1: T_{p+1,p} = -T_{p+1,p+1} (A_{p+1,p} T_{p,p}), p = 0, 32 (waves 0, 1)
+  if (wave < 2) {
+    const int p = 32 * wave;
+    const f32x4 y = tile_mm_f32<16>(&sm.A[p + 16][p], kC + 4, &sm.Tf[p][p], kC + 4, c, q4);
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) sm.Ys[16 * wave + 4 * q4 + i4][c] = y[i4];
+  }
+  __syncthreads();
+  if (wave < 2) {
+    const int p = 32 * wave;
+    const f32x4 t = tile_mm_f32<16>(&sm.Tf[p + 16][p + 16], kC + 4, &sm.Ys[16 * wave][0], 36, c, q4);
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) sm.Tf[p + 16 + 4 * q4 + i4][p + c] = -t[i4];
+  }
+  __syncthreads();
+  // level 2: T_{2:4,0:2} = -T_{2:4,2:4} (A_{2:4,0:2} T_{0:2,0:2}), one 16x16 tile per wave
+  {
+    const int yi = wave >> 1, yj = wave & 1;
+    const f32x4 y = tile_mm_f32<32>(&sm.A[32 + 16 * yi][0], kC + 4, &sm.Tf[0][16 * yj], kC + 4, c, q4);
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) sm.Ys[16 * yi + 4 * q4 + i4][16 * yj + c] = y[i4];
+  }
+  __syncthreads();
+  {
+    const int xi = wave >> 1, xj = wave & 1;
+    const f32x4 t = tile_mm_f32<32>(&sm.Tf[32 + 16 * xi][32], kC + 4, &sm.Ys[0][16 * xj], 36, c, q4);
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) sm.Tf[32 + 16 * xi + 4 * q4 + i4][16 * xj + c] = -t[i4];
+  }
+  __syncthreads();
+  // T to hi/lo bf16 over the lower 32x32-block triangle (the upper parts of
+  // the diagonal blocks are zero and are read by 32-wide steps)
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int gidx = tid + kNT * k;  // 768 groups of 4: rows 0..31 x 8, rows 32..63 x 16
+    int i, j0;
+    if (gidx < 256) {
+      i = gidx >> 3;
+      j0 = 4 * (gidx & 7);
+    } else {
+      i = 32 + ((gidx - 256) >> 4);
+      j0 = 4 * ((gidx - 256) & 15);
+    }
+    u32x2 hi, lo;
+    split4(*reinterpret_cast<const f32x4*>(&sm.Tf[i][j0]), hi, lo);
+    const int off = compact_idx(i, perm32(j0));
+    *reinterpret_cast<u32x2*>(Thg + off) = hi;
+    *reinterpret_cast<u32x2*>(Tlg + off) = lo;
   }
 }
 
-template <typename TO>
-__global__ __launch_bounds__(kNT) void chunk_bf16_kernel(ChunkArgs a) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  Smem& sm = *reinterpret_cast<Smem*>(smem_raw);
+// ---------------------------------------------------------------------------
+// Recurrence: carries the state of 64 value channels of one (sequence,
+// value head) through its chunks.
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// One chunk's shared inputs in LDS.  Each region is a whole number of 1 KiB
+// blocks, so one 64-lane direct-to-LDS load (16 bytes per lane) fills one block
+// of one region:
+//   k, q rows:  17 blocks each, 64 rows of 272 bytes (16 data slots + 1 pad)
+//   T hi, T lo, P hi, P lo: 7 blocks each; rows 0..31 hold the 32 columns the
+//               state phase reads (80-byte rows: 4 data slots + 1 pad), rows
+//               32..63 all 64 (144-byte rows: 8 + 1)
+//   factors:    2 blocks (bt, xr, yq, cL x 64 fp32, then e^{G_L})
+//   v:          10 blocks, 64 token rows of this workgroup's 64 channels
+//               (160-byte rows: 8 data slots + 2 pad)
+// Row pitches keep the row-strided fragment reads and the transposing reads
+// of the state phase free of (or low in) bank conflicts.
+constexpr int kMatLds = 7 * 1024;
+constexpr int kVRow = 80;  // v row pitch in bf16 elements
+struct __align__(16) RecBuf {
+  uint16_t Kr[kC][kD + 8];
+  uint16_t Qr[kC][kD + 8];
+  unsigned char M[4][kMatLds];
+  float fac[4][kC];
+  float eGL[4];
+  float pad_[252];
+  uint16_t V[kC][kVRow];
+};
+static_assert(sizeof(RecBuf) == 74 * 1024, "RecBuf must be 74 KiB");
+constexpr int kRecLoads = 74;      // 1 KiB blocks per buffer
+constexpr int kLoadsPerWave = 19;  // ceil(kRecLoads / 4 waves)
+
+// Byte offset of row i of an LDS T/P matrix.
+__device__ __forceinline__ int mrow(int i) { return i < 32 ? 80 * i : 2560 + 144 * (i - 32); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+
+// Direct load of block i (0..73), lane `lane`: byte offset of its source
+// relative to the k / q row base (blocks 0..33), the chunk record (34..63) or
+// the v base (64..73), and whether the lane carries data (padding and unused
+// slots stay idle).
+struct BlockSrc {
+  uint32_t off;
+  bool used;
+};
+
+__device__ __forceinline__ BlockSrc block_src(int i, int lane, int row_bytes, int vrow_bytes, int L) {
+  BlockSrc r;
+  if (i < 34) {
+    const int s = 64 * (i < 17 ? i : i - 17) + lane;  // row s/17, 16-byte column s%17
+    const int row = s / 17, ch = s - 17 * row;
+    r.off = (uint32_t)min(row, L - 1) * row_bytes + ch * 16;
+    r.used = ch < 16;
+  } else if (i < 62) {
+    const int b = i - 34, m = b / 7;
+    const int s = 64 * (b - 7 * m) + lane;  // slot within the 7 KiB matrix
+    int piece;
+    if (s < 160) {
+      const int row = s / 5, ch = s - 5 * row;
+      r.used = ch < 4;
+      piece = row * 4 + ch;
+    } else {
+      const int t = s - 160, row = t / 9, ch = t - 9 * row;
+      r.used = ch < 8;
+      piece = 128 + row * 8 + ch;
+    }
+    r.off = (uint32_t)(m * kMatBytes + piece * 16);
+  } else if (i < 64) {
+    r.off = (uint32_t)(kFacOff + (i == 62 ? 16 * lane : 1024));
+    r.used = i == 62 || lane == 0;
+  } else {
+    const int s = 64 * (i - 64) + lane;  // row s/10, 16-byte column s%10
+    const int row = s / 10, ch = s - 10 * row;
+    r.off = (uint32_t)min(row, L - 1) * vrow_bytes + ch * 16;
+    r.used = ch < 8;
+  }
+  if (!r.used) r.off = 0;
+  return r;
+}
+
+// Issue direct loads jj0 .. jj1-1 of this wave (block i = wave + 4 jj).
+__device__ __forceinline__ void rec_issue_lds(RecBuf* buf, const uint16_t* kb, const uint16_t* qb,
+                                              const unsigned char* rb, const uint16_t* vb, const BlockSrc* src,
+                                              int wave, int jj0, int jj1) {
+#pragma unroll
+  for (int jj = jj0; jj < jj1; ++jj) {
+    const int i = wave + 4 * jj;
+    if (i >= kRecLoads) break;
+    lds_void_ptr dst = (lds_void_ptr)(reinterpret_cast<unsigned char*>(buf) + 1024 * i);
+    const unsigned char* base;
+    if (i < 17) base = reinterpret_cast<const unsigned char*>(kb);
+    else if (i < 34) base = reinterpret_cast<const unsigned char*>(qb);
+    else if (i < 64) base = rb;
+    else base = reinterpret_cast<const unsigned char*>(vb);
+    if (src[jj].used) __builtin_amdgcn_global_load_lds(base + src[jj].off, dst, 16, 0, 0);
+  }
+}
+
+// Output stores of tiles ti0..ti1-1: O[ti] holds rows 16 ti + 4 q4 + i of this
+// lane's value channel; `op` points at row 4 q4 of the chunk, `ts` is the
+// token stride in elements.
+template <typename TO>
+__device__ __forceinline__ void store_out(TO* op, size_t ts, const f32x4* O, int L, int q4, int ti0, int ti1) {
+#pragma unroll
+  for (int ti = ti0; ti < ti1; ++ti) {
+    if (L == kC) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) store_from_f32(op + (16 * ti + i4) * ts, O[ti][i4]);
+    } else {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        if (16 * ti + 4 * q4 + i4 < L) store_from_f32(op + (16 * ti + i4) * ts, O[ti][i4]);
+    }
+  }
+}
+
+// bf16x8 fragment from two transposing LDS reads (rows r0..r0+3 and
+// r1..r1+3 of this lane's column, see ds_read_b64_tr_b16).
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* p0, const uint16_t* p1) {
+  const v4i16 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p0));
+  const v4i16 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p1));
+  const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
+  return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
+}
+
+template <typename TO>
+__global__ __launch_bounds__(kNT) void chunk_rec_kernel(ChunkArgs a, const unsigned char* ws) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  RecBuf* bufs = reinterpret_cast<RecBuf*>(smem_raw);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int c = lane & 15, q4 = lane >> 4;
   const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
   const int kh = h / (a.Hv / a.Hk);
-  const int v0 = slice * kDVS;
-  const int vcol = v0 + 16 * wave + c;  // this lane's value channel
-  int bos, eos;
+  const int vcol = slice * kDVS + 16 * wave + c;  // this lane's value channel
+  int bos, eos, jb;
   if (a.cu_seqlens) {
     bos = a.cu_seqlens[n];
     eos = a.cu_seqlens[n + 1];
+    jb = reinterpret_cast<const int32_t*>(ws)[n];
   } else {
     bos = n * a.T;
     eos = bos + a.T;
+    jb = n * ((a.T + kC - 1) / kC);
   }
-  TO* og = static_cast<TO*>(a.o);
+  const unsigned char* recs = ws + kTableBytes(a.N) + (size_t)h * kRecBytes;
+  const size_t rstride = (size_t)a.Hv * kRecBytes;
+  const size_t kqts = (size_t)a.Hk * kD;  // token stride of k and q (elements)
+  const size_t vts = (size_t)a.Hv * kD;   // token stride of v and o
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)kh * kD;
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (size_t)kh * kD;
+  TO* og = static_cast<TO*>(a.o) + ((size_t)(bos + 4 * q4) * a.Hv + h) * kD + vcol;
+  const int row_bytes = a.Hk * kD * 2;
+
+  const int vrow_bytes = a.Hv * kD * 2;
+  const uint16_t* vgb = static_cast<const uint16_t*>(a.v) + (size_t)h * kD + slice * kDVS;  // v row base
+
+  BlockSrc full[kLoadsPerWave];  // full-chunk sources of this lane's direct loads
+#pragma unroll
+  for (int jj = 0; jj < kLoadsPerWave; ++jj) full[jj] = block_src(wave + 4 * jj, lane, row_bytes, vrow_bytes, kC);
 
   // State S^T tiles (kd-tile kt): lane holds S[vcol][16 kt + 4 q4 + i].
   f32x4 s[8];
@@ -204,260 +594,80 @@ __global__ __launch_bounds__(kNT) void chunk_bf16_kernel(ChunkArgs a) {
     s[kt] = a.initial_state ? *reinterpret_cast<const f32x4*>(a.initial_state + sbase + 16 * kt)
                             : f32x4{0.f, 0.f, 0.f, 0.f};
 
-  ChunkRegs cur;
+  // Sources of the chunk at token cc (index jc): uniform bases + per-lane offsets.
+  const uint16_t *nk = nullptr, *nq = nullptr, *nv = nullptr;
+  const unsigned char* nr = nullptr;
+  BlockSrc nsrc[kLoadsPerWave];
+  auto prepare = [&](int cc, int jc) {
+    const int Lc = min(kC, eos - cc);
+    nk = kg + (size_t)cc * kqts;
+    nq = qg + (size_t)cc * kqts;
+    nv = vgb + (size_t)cc * vts;
+    nr = recs + (size_t)jc * rstride;
+    if (Lc < kC) {
+#pragma unroll
+      for (int jj = 0; jj < kLoadsPerWave; ++jj) nsrc[jj] = block_src(wave + 4 * jj, lane, row_bytes, vrow_bytes, Lc);
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < kLoadsPerWave; ++jj) nsrc[jj] = full[jj];
+    }
+  };
   if (bos < eos) {
-    const int L0 = min(kC, eos - bos);
-    if (L0 == kC) issue_loads<true>(cur, a, bos, L0, kh, h, vcol, tid, lane, wave, q4);
-    else issue_loads<false>(cur, a, bos, L0, kh, h, vcol, tid, lane, wave, q4);
+    prepare(bos, jb);
+    rec_issue_lds(bufs, nk, nq, nr, nv, nsrc, wave, 0, kLoadsPerWave);
   }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
-  for (int c0 = bos; c0 < eos; c0 += kC) {
+  f32x4 Oprev[4];
+  int pL = 0;
+  int it = 0;
+  for (int c0 = bos, j = jb; c0 < eos; c0 += kC, ++j, ++it) {
     const int L = min(kC, eos - c0);
-
-    // ---- store this chunk's k/q blocks to LDS (k also transposed)
-    {
-      const int b = tid & 127, rb = b >> 4, cb = b & 15;
-      uint16_t(*X)[kD + 8] = tid < 128 ? sm.Kr : sm.Qr;
-      const int pc = perm8(cb);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const u32x4 w = __builtin_bit_cast(u32x4, cur.kq[i]);
-        *reinterpret_cast<u32x2*>(&X[8 * rb + i][pc]) = u32x2{w[0], w[1]};
-        *reinterpret_cast<u32x2*>(&X[8 * rb + i][pc + 8]) = u32x2{w[2], w[3]};
-      }
-      if (tid < 128) {
-        const int pr8 = perm8(rb);
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {  // columns 2*e2, 2*e2+1 of the 8x8 block
-          uint32_t lo01[4], hi01[4];
-#pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            const uint32_t w0 = __builtin_bit_cast(u32x4, cur.kq[i])[e2];
-            const uint32_t w1 = __builtin_bit_cast(u32x4, cur.kq[i + 1])[e2];
-            lo01[i / 2] = (w0 & 0xffffu) | (w1 << 16);
-            hi01[i / 2] = (w0 >> 16) | (w1 & 0xffff0000u);
-          }
-          *reinterpret_cast<u32x2*>(&sm.Kt[8 * cb + 2 * e2][pr8]) = u32x2{lo01[0], lo01[1]};
-          *reinterpret_cast<u32x2*>(&sm.Kt[8 * cb + 2 * e2][pr8 + 8]) = u32x2{lo01[2], lo01[3]};
-          *reinterpret_cast<u32x2*>(&sm.Kt[8 * cb + 2 * e2 + 1][pr8]) = u32x2{hi01[0], hi01[1]};
-          *reinterpret_cast<u32x2*>(&sm.Kt[8 * cb + 2 * e2 + 1][pr8 + 8]) = u32x2{hi01[2], hi01[3]};
-        }
-      }
-      if (wave == 0) sm.gin[lane] = cur.gb;
-      if (wave == 1) sm.bin[lane] = cur.gb;
-    }
-    uint16_t vv[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) vv[i] = cur.vv[i];
-    __syncthreads();
-
-    // ---- Gram tiles (raw bf16 products): job 0..9 K_j K_i^T, 10..19 K_j Q_i^T,
-    // 20..23 Q_i Q_i^T (diagonal only, for the q norms).  Lane holds
-    // G[row i = 16 ti + c][cols j = 16 tj + 4 q4 .. +3].
-    f32x4 gacc[5];
-    int gti[5], gtj[5];
-#pragma unroll
-    for (int u = 0; u < 6; ++u) {
-      const int job = wave + kNW * u;
-      int ti, tj;
-      const uint16_t(*XA)[kD + 8];
-      const uint16_t(*XB)[kD + 8];
-      if (job < 20) {
-        const int idx = job % 10;
-        ti = idx >= 6 ? 3 : (idx >= 3 ? 2 : (idx >= 1 ? 1 : 0));
-        tj = idx - ti * (ti + 1) / 2;
-        XA = sm.Kr;
-        XB = job < 10 ? sm.Kr : sm.Qr;
-      } else {
-        ti = tj = job - 20;
-        XA = sm.Qr;
-        XB = sm.Qr;
-      }
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        acc = mfma16x16x32(lds8(&XA[16 * tj + c][32 * ks + 8 * q4]), lds8(&XB[16 * ti + c][32 * ks + 8 * q4]), acc);
-      if (u < 5) {
-        gacc[u] = acc;
-        gti[u] = ti;
-        gtj[u] = tj;
-      }
-      if (ti == tj && (job < 10 || job >= 20) && (c >> 2) == q4) {
-        (job < 10 ? sm.ssk : sm.ssq)[16 * ti + c] = acc[c & 3];
-      }
-    }
-    __syncthreads();
-
-    // ---- per-token factors (wave 0): norms, fp64 cumulative decay, scales
-    if (wave == 0) {
-      const float rkv = a.use_l2 ? 1.f / sqrtf(sm.ssk[lane] + a.eps) : 1.f;
-      const float rqv = a.use_l2 ? 1.f / sqrtf(sm.ssq[lane] + a.eps) : 1.f;
-      double G = (double)sm.gin[lane];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(G, off, 64);
-        if (lane >= off) G += o;
-      }
-      const float g2 = (float)(G * 1.4426950408889634);
-      const float g2L = __shfl(g2, 63, 64);
-      const float eG = exp2f(g2);
-      const float bv = sm.bin[lane];
-      sm.G2[lane] = g2;
-      sm.rk[lane] = rkv;
-      sm.ar[lane] = bv * rkv;
-      sm.pr[lane] = a.scale * rqv;
-      sm.bt[lane] = bv;
-      sm.xr[lane] = bv * eG * rkv;
-      sm.yq[lane] = a.scale * rqv * eG;
-      sm.cL[lane] = rkv * exp2f(g2L - g2);
-      if (lane == 0) sm.eGL = exp2f(g2L);
-    }
-    __syncthreads();
-
-    // ---- scale Gram tiles into A (fp32) and P (hi/lo bf16)
-#pragma unroll
-    for (int u = 0; u < 5; ++u) {
-      const int job = wave + kNW * u;
-      if (job >= 20) break;
-      const int ti = gti[u], tj = gtj[u];
-      const int i = 16 * ti + c, j0 = 16 * tj + 4 * q4;
-      const float g2i = sm.G2[i];
-      const f32x4 g2j = *reinterpret_cast<const f32x4*>(&sm.G2[j0]);
-      const f32x4 rkj = *reinterpret_cast<const f32x4*>(&sm.rk[j0]);
-      const float rowf = job < 10 ? sm.ar[i] : sm.pr[i];
-      f32x4 val;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + e;
-        const bool keep = job < 10 ? (j < i) : (j <= i);
-        val[e] = keep ? rowf * rkj[e] * exp2f(g2i - g2j[e]) * gacc[u][e] : 0.f;
-      }
-      if (job < 10) {
-        *reinterpret_cast<f32x4*>(&sm.A[i][j0]) = val;
-      } else {
-        u32x2 hi, lo;
-        split4(val, hi, lo);
-        const int pj = perm32(j0);
-        *reinterpret_cast<u32x2*>(&sm.Ph[i][pj]) = hi;
-        *reinterpret_cast<u32x2*>(&sm.Pl[i][pj]) = lo;
-      }
-    }
-    // zero the above-diagonal tiles (0,1) and (2,3) that 32-wide steps read
-    if (wave < 2) {
-      const int i = 32 * wave + c, pj = perm32(32 * wave + 16 + 4 * q4);
-      *reinterpret_cast<u32x2*>(&sm.Ph[i][pj]) = u32x2{0u, 0u};
-      *reinterpret_cast<u32x2*>(&sm.Pl[i][pj]) = u32x2{0u, 0u};
-      *reinterpret_cast<f32x4*>(&sm.Tf[i][32 * wave + 16 + 4 * q4]) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    __syncthreads();
-
-    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution
-    // (wave w inverts block w; lane c < 16 computes column c)
-    if (lane < 16) {
-      const int b = wave;
-      float x[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        const float* arow = &sm.A[16 * b + r][16 * b];
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int m4 = 0; m4 < r; m4 += 4) {
-          const f32x4 av = *reinterpret_cast<const f32x4*>(arow + m4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (m4 + e < r) {
-              if (e & 1) s1 += av[e] * x[m4 + e];
-              else s0 += av[e] * x[m4 + e];
-            }
-        }
-        x[r] = (r > c) ? -(s0 + s1) : x[r];
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sm.Tf[16 * b + r][16 * b + c] = x[r];
-    }
-    __syncthreads();
-    // level 1: T_{p+1,p} = -T_{p+1,p+1} (A_{p+1,p} T_{p,p}), p = 0, 32 (waves 0, 1)
-    if (wave < 2) {
-      const int p = 32 * wave;
-      const f32x4 y = tile_mm_f32<16>(&sm.A[p + 16][p], kC + 4, &sm.Tf[p][p], kC + 4, c, q4);
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) sm.Ys[16 * wave + 4 * q4 + i4][c] = y[i4];
-    }
-    __syncthreads();
-    if (wave < 2) {
-      const int p = 32 * wave;
-      const f32x4 t = tile_mm_f32<16>(&sm.Tf[p + 16][p + 16], kC + 4, &sm.Ys[16 * wave][0], 36, c, q4);
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) sm.Tf[p + 16 + 4 * q4 + i4][p + c] = -t[i4];
-    }
-    __syncthreads();
-    // level 2: T_{2:4,0:2} = -T_{2:4,2:4} (A_{2:4,0:2} T_{0:2,0:2}), one 16x16 tile per wave
-    {
-      const int yi = wave >> 1, yj = wave & 1;
-      const f32x4 y = tile_mm_f32<32>(&sm.A[32 + 16 * yi][0], kC + 4, &sm.Tf[0][16 * yj], kC + 4, c, q4);
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) sm.Ys[16 * yi + 4 * q4 + i4][16 * yj + c] = y[i4];
-    }
-    __syncthreads();
-    {
-      const int xi = wave >> 1, xj = wave & 1;
-      const f32x4 t = tile_mm_f32<32>(&sm.Tf[32 + 16 * xi][32], kC + 4, &sm.Ys[0][16 * xj], 36, c, q4);
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) sm.Tf[32 + 16 * xi + 4 * q4 + i4][16 * xj + c] = -t[i4];
-    }
-    __syncthreads();
-    // T to hi/lo bf16 over the lower 32x32-block triangle (the upper parts of
-    // the diagonal blocks are zero and are read by 32-wide steps)
-#pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int gidx = tid + kNT * k;  // 768 groups of 4: rows 0..31 x 8, rows 32..63 x 16
-      int i, j0;
-      if (gidx < 256) {
-        i = gidx >> 3;
-        j0 = 4 * (gidx & 7);
-      } else {
-        i = 32 + ((gidx - 256) >> 4);
-        j0 = 4 * ((gidx - 256) & 15);
-      }
-      u32x2 hi, lo;
-      split4(*reinterpret_cast<const f32x4*>(&sm.Tf[i][j0]), hi, lo);
-      const int pj = perm32(j0);
-      *reinterpret_cast<u32x2*>(&sm.Th[i][pj]) = hi;
-      *reinterpret_cast<u32x2*>(&sm.Tl[i][pj]) = lo;
-    }
-
-    // ---- prefetch the next chunk's inputs while this one finishes
-    ChunkRegs nxt;
-    const int c1 = c0 + kC;
-    if (c1 < eos) {
-      const int L1 = min(kC, eos - c1);
-      if (L1 == kC) issue_loads<true>(nxt, a, c1, L1, kh, h, vcol, tid, lane, wave, q4);
-      else issue_loads<false>(nxt, a, c1, L1, kh, h, vcol, tid, lane, wave, q4);
-    }
-    __syncthreads();
+    RecBuf& B = bufs[it & 1];
+    RecBuf* NB = bufs + ((it & 1) ^ 1);
+    const bool more = c0 + kC < eos;
+    if (more) prepare(c0 + kC, j + 1);
+    TO* oprev = og + (size_t)(c0 - kC - bos) * vts;
+    if (more) rec_issue_lds(NB, nk, nq, nr, nv, nsrc, wave, 0, 5);
+    if (it > 0) store_out(oprev, vts, Oprev, pL, q4, 0, 1);
 
     // ---- state phase: this wave's 16 value channels
     bf16x8 sbh[4], sbl[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) split8(s[2 * ks], s[2 * ks + 1], sbh[ks], sbl[ks]);
 
-    f32x4 R[4];
+    f32x4 R[4], Y[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 ak = lds8(&sm.Kr[16 * ti + c][32 * ks + 8 * q4]);
+        const uint16_t* kr = &B.Kr[16 * ti + c][32 * ks + 4 * q4];
+        const uint16_t* qr = &B.Qr[16 * ti + c][32 * ks + 4 * q4];
+        const u32x2 k0 = *reinterpret_cast<const u32x2*>(kr), k1 = *reinterpret_cast<const u32x2*>(kr + 16);
+        const u32x2 q0 = *reinterpret_cast<const u32x2*>(qr), q1 = *reinterpret_cast<const u32x2*>(qr + 16);
+        const bf16x8 ak = __builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]});
+        const bf16x8 aq = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
         acc = mfma16x16x32(ak, sbh[ks], acc);
+        y = mfma16x16x32(aq, sbh[ks], y);
         acc = mfma16x16x32(ak, sbl[ks], acc);
+        y = mfma16x16x32(aq, sbl[ks], y);
       }
-      const f32x4 btv = *reinterpret_cast<const f32x4*>(&sm.bt[16 * ti + 4 * q4]);
-      const f32x4 xrv = *reinterpret_cast<const f32x4*>(&sm.xr[16 * ti + 4 * q4]);
+      // v[16 ti + 4 q4 + e][vcol], e = 0..3, by one transposing read
+      const v4i16 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_ptr)(&B.V[16 * ti + 4 * q4 + (c >> 2)][16 * wave + 4 * (c & 3)]));
+      const f32x4 btv = *reinterpret_cast<const f32x4*>(&B.fac[0][16 * ti + 4 * q4]);
+      const f32x4 xrv = *reinterpret_cast<const f32x4*>(&B.fac[1][16 * ti + 4 * q4]);
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) R[ti][i4] = btv[i4] * bf16_to_f32(vv[4 * ti + i4]) - xrv[i4] * acc[i4];
+      for (int i4 = 0; i4 < 4; ++i4)
+        R[ti][i4] = btv[i4] * __uint_as_float((uint32_t)(uint16_t)vt[i4] << 16) - xrv[i4] * acc[i4];
+      Y[ti] = y * *reinterpret_cast<const f32x4*>(&B.fac[2][16 * ti + 4 * q4]);
     }
+    if (more) rec_issue_lds(NB, nk, nq, nr, nv, nsrc, wave, 5, 10);
+    if (it > 0) store_out(oprev, vts, Oprev, pL, q4, 1, 2);
+
     bf16x8 rbh[2], rbl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) split8(R[2 * ks], R[2 * ks + 1], rbh[ks], rbl[ks]);
@@ -466,11 +676,13 @@ __global__ __launch_bounds__(kNT) void chunk_bf16_kernel(ChunkArgs a) {
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int ro = mrow(16 * ti + c);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         if (2 * ks > ti) continue;
-        acc = mfma3(lds8(&sm.Th[16 * ti + c][32 * ks + 8 * q4]), lds8(&sm.Tl[16 * ti + c][32 * ks + 8 * q4]),
-                    rbh[ks], rbl[ks], acc);
+        const int off = ro + 2 * (32 * ks + 8 * q4);
+        acc = mfma3(lds8(reinterpret_cast<const uint16_t*>(&B.M[0][off])),
+                    lds8(reinterpret_cast<const uint16_t*>(&B.M[1][off])), rbh[ks], rbl[ks], acc);
       }
       Dl[ti] = acc;
     }
@@ -478,56 +690,50 @@ __global__ __launch_bounds__(kNT) void chunk_bf16_kernel(ChunkArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       split8(Dl[2 * ks], Dl[2 * ks + 1], dbh[ks], dbl[ks]);
-      const f32x4 cl0 = *reinterpret_cast<const f32x4*>(&sm.cL[32 * ks + 4 * q4]);
-      const f32x4 cl1 = *reinterpret_cast<const f32x4*>(&sm.cL[32 * ks + 16 + 4 * q4]);
+      const f32x4 cl0 = *reinterpret_cast<const f32x4*>(&B.fac[3][32 * ks + 4 * q4]);
+      const f32x4 cl1 = *reinterpret_cast<const f32x4*>(&B.fac[3][32 * ks + 16 + 4 * q4]);
       split8(Dl[2 * ks] * cl0, Dl[2 * ks + 1] * cl1, dph[ks], dpl[ks]);
     }
+    if (more) rec_issue_lds(NB, nk, nq, nr, nv, nsrc, wave, 10, 15);
+    if (it > 0) store_out(oprev, vts, Oprev, pL, q4, 2, 4);
 
-    // outputs O = yq * (Q S0^T) + P Delta
+    // outputs O = yq * (Q S0^T) + P Delta (stored during the next chunk)
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 aq = lds8(&sm.Qr[16 * ti + c][32 * ks + 8 * q4]);
-        y = mfma16x16x32(aq, sbh[ks], y);
-        y = mfma16x16x32(aq, sbl[ks], y);
-      }
-      y = y * *reinterpret_cast<const f32x4*>(&sm.yq[16 * ti + 4 * q4]);
+      f32x4 y = Y[ti];
+      const int ro = mrow(16 * ti + c);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         if (2 * ks > ti) continue;
-        y = mfma3(lds8(&sm.Ph[16 * ti + c][32 * ks + 8 * q4]), lds8(&sm.Pl[16 * ti + c][32 * ks + 8 * q4]),
-                  dbh[ks], dbl[ks], y);
+        const int off = ro + 2 * (32 * ks + 8 * q4);
+        y = mfma3(lds8(reinterpret_cast<const uint16_t*>(&B.M[2][off])),
+                  lds8(reinterpret_cast<const uint16_t*>(&B.M[3][off])), dbh[ks], dbl[ks], y);
       }
-      TO* op = og + ((size_t)(c0 + 16 * ti + 4 * q4) * a.Hv + h) * kD + vcol;
-      const size_t ts = (size_t)a.Hv * kD;
-      if (L == kC) {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) store_from_f32(op + i4 * ts, y[i4]);
-      } else {
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4)
-          if (16 * ti + 4 * q4 + i4 < L) store_from_f32(op + i4 * ts, y[i4]);
-      }
+      Oprev[ti] = y;
     }
+    if (more) rec_issue_lds(NB, nk, nq, nr, nv, nsrc, wave, 15, kLoadsPerWave);
 
-    // state update S^T <- e^{G_L} S^T + K^T Delta'
-    const float eGL = sm.eGL;
+    // state update S^T <- e^{G_L} S^T + K^T Delta'; K^T fragments by
+    // transposing reads of the row-major k tile (last: the compiler waits for
+    // the prefetch before these reads)
+    const float eGL = B.eGL[0];
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt) {
       f32x4 acc = s[kt] * eGL;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 akt = lds8(&sm.Kt[16 * kt + c][32 * ks + 8 * q4]);
+        const int r0 = 32 * ks + 4 * q4 + (c >> 2), col = 16 * kt + 4 * (c & 3);
+        const bf16x8 akt = tr_frag(&B.Kr[r0][col], &B.Kr[r0 + 16][col]);
         acc = mfma16x16x32(akt, dph[ks], acc);
         acc = mfma16x16x32(akt, dpl[ks], acc);
       }
       s[kt] = acc;
     }
-    cur = nxt;
+    pL = L;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  if (it > 0) store_out(og + (size_t)(eos - pL - bos) * vts, vts, Oprev, pL, q4, 0, 4);
 
   if (a.final_state) {
 #pragma unroll
@@ -536,20 +742,46 @@ __global__ __launch_bounds__(kNT) void chunk_bf16_kernel(ChunkArgs a) {
 }
 
 template <typename TO>
-hipError_t launch_bf16_t(const ChunkArgs& a, hipStream_t st) {
-  auto kern = chunk_bf16_kernel<TO>;
-  const size_t smem = sizeof(Smem);
+hipError_t launch_rec_t(const ChunkArgs& a, const unsigned char* ws, hipStream_t st) {
+  auto kern = chunk_rec_kernel<TO>;
+  const size_t smem = 2 * sizeof(RecBuf);  // 148 KiB: double-buffered chunk inputs
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(kD / kDVS, a.Hv, a.N), dim3(kNT), smem, st, a);
+  hipLaunchKernelGGL(kern, dim3(kD / kDVS, a.Hv, a.N), dim3(kNT), smem, st, a, ws);
   return hipGetLastError();
+}
+
+size_t max_chunks(const ChunkArgs& a) {
+  const size_t per = ((size_t)a.T + kC - 1) / kC;
+  return a.cu_seqlens ? per + (size_t)a.N : per * (size_t)a.N;
 }
 
 }  // namespace
 
-hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t st) {
-  return a.out_bf16 ? launch_bf16_t<uint16_t>(a, st) : launch_bf16_t<float>(a, st);
+size_t chunk_bf16_workspace_bytes(const ChunkArgs& a) {
+  return kTableBytes(a.N) + max_chunks(a) * (size_t)a.Hv * kRecBytes;
+}
+
+hipError_t launch_chunk_bf16(const ChunkArgs& a, void* workspace, hipStream_t st) {
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if (a.cu_seqlens) {
+    hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.N,
+                       reinterpret_cast<int32_t*>(ws));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const size_t nch = max_chunks(a);
+  if (nch > 0) {
+    const size_t smem = sizeof(PrepSmem);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_prep_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)nch, a.Hv), dim3(kNT), smem, st, a, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return a.out_bf16 ? launch_rec_t<uint16_t>(a, ws, st) : launch_rec_t<float>(a, ws, st);
 }
 
 }  // namespace gdr

@@ -56,13 +56,15 @@ def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
                            use_qk_l2norm_in_kernel: bool = True, scale: float = 1.0,
                            chunk_size: int = 64, out_dtype: torch.dtype = torch.float32,
                            final_state: Optional[torch.Tensor] = None,
-                           out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                           out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked prefill (gdr_chunk_fwd).
 
     q, k: [B, T, Hk, d]; v: [B, T, Hv, d] (bf16 or fp32, same dtype);
     g, beta: [B, T, Hv] fp32; initial_state: [N, Hv, d, d] fp32 or None;
     cu_seqlens: int32 [N+1] (then B must be 1).  ``final_state`` may be given
-    as a preallocated output (it may be ``initial_state`` itself).
+    as a preallocated output (it may be ``initial_state`` itself); ``workspace``
+    (uint8, device) is used if large enough, else one is allocated.
     Returns (o [B, T, Hv, d] out_dtype, final_state or None).
     """
     dev = q.device
@@ -100,9 +102,14 @@ def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
         _need(out, "out", (out_dtype,), dev)
     desc = make_desc(B, T, N, Hk, Hv, D, chunk_size, qd, out_dtype, use_qk_l2norm_in_kernel, scale, 1e-6)
     lib = _lib.load()
+    nbytes = ctypes.c_size_t(0)
+    _lib.check("gdr_chunk_fwd_workspace_size", lib.gdr_chunk_fwd_workspace_size(ctypes.byref(desc),
+                                                                                ctypes.byref(nbytes)))
+    if workspace is None or workspace.numel() < nbytes.value:
+        workspace = torch.empty(nbytes.value, device=dev, dtype=torch.uint8) if nbytes.value else None
     st = lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                            _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(out),
-                           None, 0, _stream(dev))
+                           _ptr(workspace), nbytes.value, _stream(dev))
     _lib.check("gdr_chunk_fwd", st)
     return out, final_state
 

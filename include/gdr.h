@@ -99,8 +99,14 @@ const char* gdr_status_string(int status);
 const char* gdr_last_error(void);
 
 /*
- * Device workspace that gdr_chunk_fwd needs for descriptor *d, in bytes
- * (currently 0 for every supported shape; callers may then pass NULL).
+ * Device workspace that gdr_chunk_fwd needs for descriptor *d, in bytes.
+ * The bf16-MFMA path (bf16 q/k/v, d = 128, chunk 64) stores a chunk table
+ * (N+1 int32, padded to 256 bytes) and one 25728-byte record per (chunk,
+ * value head) -- the chunk's T = (I+A)^{-1} and P as bf16 hi/lo pairs and its
+ * per-token factors -- for an upper bound of ceil(T/64) + N chunks when
+ * batch == 1 (packed or single sequence) and B * ceil(T/64) otherwise.  Every
+ * other combination needs 0 bytes (workspace may then be NULL).  The
+ * contents need no initialisation and are dead after the call returns.
  * Errors: INVALID_ARG / UNSUPPORTED as gdr_chunk_fwd would report them.
  */
 gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* d, size_t* bytes);
@@ -120,7 +126,9 @@ gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* d, size_t* bytes);
  *                 cu[N] = T; sequence n is tokens [cu[n], cu[n+1]) of the
  *                 single packed row.  NULL = B independent rows of T tokens.
  *   o             [B, T, Hv, d_v]  out_dtype output (never aliases inputs)
- *   workspace     device buffer of gdr_chunk_fwd_workspace_size() bytes
+ *   workspace     device buffer of at least gdr_chunk_fwd_workspace_size()
+ *                 bytes, 16-byte aligned (INVALID_ARG if missing or short);
+ *                 used by the kernels of this call only
  *
  * Supported: d_k = d_v in {32, 64, 128}; chunk_size 64 or 32; qkv bf16 with
  * d = 128 and chunk 64 takes the bf16-MFMA path, every other supported

@@ -90,8 +90,18 @@ def test_chunk_fwd_rejects_null_and_misaligned():
 def test_workspace_size():
     lib = _lib.load()
     n = ctypes.c_size_t(123)
-    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc()), ctypes.byref(n)) == 0 and n.value == 0
-    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc(batch=1, num_seqs=8)), ctypes.byref(n)) == 0
+    rec, table = 25728, 256
+    # bf16, d = 128, chunk 64: chunk table + one record per (chunk, value head)
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc()), ctypes.byref(n)) == 0
+    assert n.value == table + (2 + 1) * 48 * rec  # T = 128: 2 chunks, + 1 for a packed batch
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc(batch=1, num_seqs=8, seq_len=1000)),
+                                            ctypes.byref(n)) == 0
+    assert n.value == table + (16 + 8) * 48 * rec
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc(batch=3, num_seqs=3)), ctypes.byref(n)) == 0
+    assert n.value == table + 3 * 2 * 48 * rec
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc(qkv_dtype=0)), ctypes.byref(n)) == 0 and n.value == 0
+    # a call that needs a workspace and gets none fails before any launch
+    assert _chunk(_desc()) == -1 and "workspace" in lib.gdr_last_error().decode()
     assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc(chunk_size=16)), ctypes.byref(n)) == -2
     assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(_desc()), None) == -1
 
