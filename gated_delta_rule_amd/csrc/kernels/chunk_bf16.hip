@@ -42,7 +42,7 @@ namespace {
 constexpr int kD = 128;  // head dim (d_k = d_v)
 constexpr int kC = 64;   // chunk
 constexpr int kNT = 256;  // threads per workgroup (4 waves)
-constexpr int kDVS = 64;  // value channels per recurrence workgroup
+constexpr int kDVS = 32;  // value channels per recurrence workgroup
 
 // Workspace record of one (chunk, value head), in bytes: T hi, T lo, P hi,
 // P lo (each: rows 0..31 x 32 columns, then rows 32..63 x 64 columns, bf16,
@@ -69,8 +69,15 @@ __device__ __forceinline__ int perm32(int x) {
 __device__ __forceinline__ int perm8(int b) {
   return 32 * (b >> 2) + ((0x14041000u >> (8 * (b & 3))) & 0xff);
 }
-// Element offset of (row i, physical column p) in a compact T/P matrix.
-__device__ __forceinline__ int compact_idx(int i, int p) { return i < 32 ? i * 32 + p : 1024 + (i - 32) * 64 + p; }
+// Element offset of (row i, physical column p) in a compact T/P matrix: rows
+// 0..31 hold 32 columns (four 16-byte slots), rows 32..63 all 64 (eight);
+// slot s of row i is stored at s ^ ((i >> 1) & 3), resp. s ^ (i & 7), so
+// that the recurrence's fragment reads (lanes on 16 consecutive rows, one
+// slot each) hit distinct LDS banks when the record is copied to LDS as is.
+__device__ __forceinline__ int compact_idx(int i, int p) {
+  return i < 32 ? i * 32 + 8 * ((p >> 3) ^ ((i >> 1) & 3)) + (p & 7)
+                : 1024 + (i - 32) * 64 + 8 * ((p >> 3) ^ (i & 7)) + (p & 7);
+}
 
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
@@ -424,140 +431,179 @@ __global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigne
 }
 
 // ---------------------------------------------------------------------------
-// Recurrence: carries the state of 64 value channels of one (sequence,
-// value head) through its chunks.
+// Recurrence: carries the state of 32 value channels of one (sequence,
+// value head) through its chunks; wave w of the two owns 16 of them.
 
-// One chunk's shared inputs in LDS.  Each region is a whole number of 1 KiB
-// blocks, so one 64-lane direct-to-LDS load (16 bytes per lane) fills one block
-// of one region:
-//   k, q rows:  17 blocks each, 64 rows of 272 bytes (16 data slots + 1 pad)
-//   T hi, T lo, P hi, P lo: 7 blocks each; rows 0..31 hold the 32 columns the
-//               state phase reads (80-byte rows: 4 data slots + 1 pad), rows
-//               32..63 all 64 (144-byte rows: 8 + 1)
-//   factors:    2 blocks (bt, xr, yq, cL x 64 fp32, then e^{G_L})
-//   v:          10 blocks, 64 token rows of this workgroup's 64 channels
-//               (160-byte rows: 8 data slots + 2 pad)
-// Row pitches keep the row-strided fragment reads and the transposing reads
-// of the state phase free of (or low in) bank conflicts.
-constexpr int kMatLds = 7 * 1024;
-constexpr int kVRow = 80;  // v row pitch in bf16 elements
+constexpr int kRecNT = 128;  // threads per recurrence workgroup (2 waves)
+constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, one L2 each
+
+// One chunk's shared inputs in LDS (62 KiB; two buffers).  Every region is a
+// whole number of 1 KiB blocks, so one 64-lane direct-to-LDS load (16 bytes
+// per lane) fills one block:
+//   K, Q (16 blocks each): 64 rows x 256 bytes; 16-byte slot s of row r is
+//        kept at slot s ^ kqswz(r), which makes the row-strided fragment reads
+//        and the transposing reads of the state phase conflict-free
+//   M (24): the record's T hi, T lo, P hi, P lo, byte for byte (the record
+//        itself is laid out for these reads, see compact_idx)
+//   fac (2): bt, xr, yq, cL (fp32 x 64), then e^{G_L}
+//   V (4): 64 token rows of this workgroup's 32 value channels
 struct __align__(16) RecBuf {
-  uint16_t Kr[kC][kD + 8];
-  uint16_t Qr[kC][kD + 8];
-  unsigned char M[4][kMatLds];
+  uint16_t K[kC][kD];
+  uint16_t Q[kC][kD];
+  unsigned char M[4 * kMatBytes];
   float fac[4][kC];
   float eGL[4];
   float pad_[252];
-  uint16_t V[kC][kVRow];
+  uint16_t V[kC][kDVS];
 };
-static_assert(sizeof(RecBuf) == 74 * 1024, "RecBuf must be 74 KiB");
-constexpr int kRecLoads = 74;      // 1 KiB blocks per buffer
-constexpr int kLoadsPerWave = 19;  // ceil(kRecLoads / 4 waves)
+static_assert(sizeof(RecBuf) == 62 * 1024, "RecBuf must be 62 KiB");
+constexpr int kRecLoads = 62;      // 1 KiB blocks per buffer
+constexpr int kLoadsPerWave = 31;  // block i = wave + 2 jj
+constexpr int kBlkQ = 16, kBlkM = 32, kBlkF = 56, kBlkV = 58;  // region starts
+static_assert(kBlkQ % 2 == 0 && kBlkM % 2 == 0 && kBlkF % 2 == 0 && kBlkV % 2 == 0,
+              "a pair of blocks never straddles two regions");
 
-// Byte offset of row i of an LDS T/P matrix.
-__device__ __forceinline__ int mrow(int i) { return i < 32 ? 80 * i : 2560 + 144 * (i - 32); }
+// Slot swizzle of k / q row r.
+__device__ __forceinline__ int kqswz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
-// Direct load of block i (0..73), lane `lane`: byte offset of its source
-// relative to the k / q row base (blocks 0..33), the chunk record (34..63) or
-// the v base (64..73), and whether the lane carries data (padding and unused
-// slots stay idle).
-struct BlockSrc {
-  uint32_t off;
-  bool used;
+// Per-lane parts of the direct-load source offsets (bytes).
+struct RecLane {
+  uint32_t kq_e, kq_o;  // k/q block b: row 4b + lane/16, slot (lane%16) ^ kqswz(row); b%4 = wave, wave + 2
+  uint32_t slot0;       // (lane%16) ^ 4 (lane/16)
+  uint32_t lane16;      // 16 lane
+  uint32_t fac;         // factor blocks: 16 lane (wave 0), 16 min(lane, 7) (wave 1: e^{G_L} only)
+  uint32_t v;           // v block b: row 16b + lane/4, slot lane%4
 };
 
-__device__ __forceinline__ BlockSrc block_src(int i, int lane, int row_bytes, int vrow_bytes, int L) {
-  BlockSrc r;
-  if (i < 34) {
-    const int s = 64 * (i < 17 ? i : i - 17) + lane;  // row s/17, 16-byte column s%17
-    const int row = s / 17, ch = s - 17 * row;
-    r.off = (uint32_t)min(row, L - 1) * row_bytes + ch * 16;
-    r.used = ch < 16;
-  } else if (i < 62) {
-    const int b = i - 34, m = b / 7;
-    const int s = 64 * (b - 7 * m) + lane;  // slot within the 7 KiB matrix
-    int piece;
-    if (s < 160) {
-      const int row = s / 5, ch = s - 5 * row;
-      r.used = ch < 4;
-      piece = row * 4 + ch;
-    } else {
-      const int t = s - 160, row = t / 9, ch = t - 9 * row;
-      r.used = ch < 8;
-      piece = 128 + row * 8 + ch;
-    }
-    r.off = (uint32_t)(m * kMatBytes + piece * 16);
-  } else if (i < 64) {
-    r.off = (uint32_t)(kFacOff + (i == 62 ? 16 * lane : 1024));
-    r.used = i == 62 || lane == 0;
-  } else {
-    const int s = 64 * (i - 64) + lane;  // row s/10, 16-byte column s%10
-    const int row = s / 10, ch = s - 10 * row;
-    r.off = (uint32_t)min(row, L - 1) * vrow_bytes + ch * 16;
-    r.used = ch < 8;
-  }
-  if (!r.used) r.off = 0;
-  return r;
-}
-
-// Issue direct loads jj0 .. jj1-1 of this wave (block i = wave + 4 jj).
-__device__ __forceinline__ void rec_issue_lds(RecBuf* buf, const uint16_t* kb, const uint16_t* qb,
-                                              const unsigned char* rb, const uint16_t* vb, const BlockSrc* src,
-                                              int wave, int jj0, int jj1) {
+// Issue this wave's direct loads jj0..jj1-1 of one chunk into buf.  kb, qb,
+// vb point at row 0 of the chunk (k, q of the key head; this workgroup's v
+// channels), rb at the chunk record.  kFull: a whole chunk; otherwise rows at
+// or past L repeat row L-1 (they are never used, but must be finite).
+template <bool kFull>
+__device__ __forceinline__ void rec_issue(RecBuf* buf, const unsigned char* kb, const unsigned char* qb,
+                                          const unsigned char* rb, const unsigned char* vb, const RecLane& ln,
+                                          int wave, int lane, int row_bytes, int vrow_bytes, int L, int jj0,
+                                          int jj1) {
 #pragma unroll
-  for (int jj = jj0; jj < jj1; ++jj) {
-    const int i = wave + 4 * jj;
-    if (i >= kRecLoads) break;
+  for (int jj = 0; jj < kLoadsPerWave; ++jj) {
+    if (jj < jj0 || jj >= jj1) continue;
+    const int i = wave + 2 * jj;
+    const unsigned char* src;
+    uint32_t off;
+    if (2 * jj < kBlkM) {  // k or q: block b covers rows 4b .. 4b+3
+      const int b = 2 * jj < kBlkQ ? i : i - kBlkQ;
+      const unsigned char* base = 2 * jj < kBlkQ ? kb : qb;
+      if (kFull) {
+        src = base + (size_t)(4 * b) * row_bytes;
+        off = (jj & 1) ? ln.kq_o : ln.kq_e;
+      } else {
+        const int row = min(4 * b + (lane >> 4), L - 1);
+        src = base;
+        off = (uint32_t)row * row_bytes + 16 * (ln.slot0 ^ (uint32_t)(b & 3));
+      }
+    } else if (2 * jj < kBlkF) {
+      src = rb + 1024 * (i - kBlkM);
+      off = ln.lane16;
+    } else if (2 * jj < kBlkV) {
+      src = rb + kFacOff + 1024 * wave;
+      off = ln.fac;
+    } else {
+      const int b = i - kBlkV;
+      if (kFull) {
+        src = vb + (size_t)(16 * b) * vrow_bytes;
+        off = ln.v;
+      } else {
+        const int row = min(16 * b + (lane >> 2), L - 1);
+        src = vb;
+        off = (uint32_t)row * vrow_bytes + 16 * (lane & 3);
+      }
+    }
     lds_void_ptr dst = (lds_void_ptr)(reinterpret_cast<unsigned char*>(buf) + 1024 * i);
-    const unsigned char* base;
-    if (i < 17) base = reinterpret_cast<const unsigned char*>(kb);
-    else if (i < 34) base = reinterpret_cast<const unsigned char*>(qb);
-    else if (i < 64) base = rb;
-    else base = reinterpret_cast<const unsigned char*>(vb);
-    if (src[jj].used) __builtin_amdgcn_global_load_lds(base + src[jj].off, dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src + off, dst, 16, 0, 0);
   }
 }
 
-// Output stores of tiles ti0..ti1-1: O[ti] holds rows 16 ti + 4 q4 + i of this
-// lane's value channel; `op` points at row 4 q4 of the chunk, `ts` is the
-// token stride in elements.
+// Output stores of tiles ti0..ti1-1 of one chunk: Ot[ti][i] is the output of
+// token 16 ti + c at value channel 4 q4 + i of this wave's 16, so each lane
+// stores 4 adjacent channels; `op` points at token c, channel 4 q4 of the
+// chunk, `ts` is the token stride in elements; tokens at or past L are skipped.
+__device__ __forceinline__ void store4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store4(uint16_t* p, const f32x4& v) {
+  *reinterpret_cast<u16x4*>(p) = u16x4{f32_to_bf16(v[0]), f32_to_bf16(v[1]), f32_to_bf16(v[2]), f32_to_bf16(v[3])};
+}
 template <typename TO>
-__device__ __forceinline__ void store_out(TO* op, size_t ts, const f32x4* O, int L, int q4, int ti0, int ti1) {
+__device__ __forceinline__ void store_out(TO* op, size_t ts, const f32x4* Ot, int L, int c, int ti0, int ti1) {
 #pragma unroll
-  for (int ti = ti0; ti < ti1; ++ti) {
-    if (L == kC) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) store_from_f32(op + (16 * ti + i4) * ts, O[ti][i4]);
-    } else {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        if (16 * ti + 4 * q4 + i4 < L) store_from_f32(op + (16 * ti + i4) * ts, O[ti][i4]);
-    }
-  }
+  for (int ti = ti0; ti < ti1; ++ti)
+    if (L == kC || 16 * ti + c < L) store4(op + (size_t)(16 * ti) * ts, Ot[ti]);
 }
 
-// bf16x8 fragment from two transposing LDS reads (rows r0..r0+3 and
-// r1..r1+3 of this lane's column, see ds_read_b64_tr_b16).
-__device__ __forceinline__ bf16x8 tr_frag(const uint16_t* p0, const uint16_t* p1) {
-  const v4i16 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p0));
-  const v4i16 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(p1));
+// bf16x8 fragment from two transposing LDS reads at byte offsets o0, o1 of
+// the buffer (see ds_read_b64_tr_b16).
+__device__ __forceinline__ bf16x8 tr_frag(const unsigned char* base, int o0, int o1) {
+  const v4i16 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + o0));
+  const v4i16 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + o1));
   const u32x2 w0 = __builtin_bit_cast(u32x2, t0), w1 = __builtin_bit_cast(u32x2, t1);
   return __builtin_bit_cast(bf16x8, u32x4{w0[0], w0[1], w1[0], w1[1]});
 }
 
+// State update of one chunk for this wave's 16 value channels:
+// S^T <- e^{G_L} S^T + K^T Delta'.  Output tile kt = 2 ks + hh holds key
+// channels 32 ks + 8 q4 + 4 hh + i, so that two tiles side by side give each
+// lane 8 adjacent key channels (one 16-byte k fragment read in the next
+// chunk).  The K^T fragments come from transposing reads of the k tile:
+// lane (c, q4) of the 16-lane group reads row 4 q4 + c/4 (+16, +32 ks2) at
+// key channels 32 ks + 8 (c%4) + 4 hh .. +3; tro[ks] holds the swizzled byte
+// offset of that piece without the row terms common to all lanes.
+__device__ __forceinline__ void state_update(f32x4* s, const RecBuf& B, const bf16x8* dph, const bf16x8* dpl,
+                                             const int* tro) {
+  const float eGL = B.eGL[0];
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(&B.K[0][0]);
+  // fragments of tile kt + 1 are read while tile kt multiplies
+  auto frag = [&](int kt, int ks2) {
+    const int o = tro[kt >> 1] + 8 * (kt & 1) + 256 * 32 * ks2;
+    return tr_frag(kbase, o, o + 256 * 16);
+  };
+  bf16x8 f[2][2];
+  f[0][0] = frag(0, 0);
+  f[0][1] = frag(0, 1);
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) {
+    if (kt < 7) {
+      f[(kt + 1) & 1][0] = frag(kt + 1, 0);
+      f[(kt + 1) & 1][1] = frag(kt + 1, 1);
+    }
+    f32x4 acc = s[kt] * eGL;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      acc = mfma16x16x32(f[kt & 1][ks2], dph[ks2], acc);
+      acc = mfma16x16x32(f[kt & 1][ks2], dpl[ks2], acc);
+    }
+    s[kt] = acc;
+  }
+}
+
 template <typename TO>
-__global__ __launch_bounds__(kNT) void chunk_rec_kernel(ChunkArgs a, const unsigned char* ws) {
+__global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const unsigned char* ws) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   RecBuf* bufs = reinterpret_cast<RecBuf*>(smem_raw);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int c = lane & 15, q4 = lane >> 4;
-  const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+  // Workgroup -> (sequence, value head, slice), XCD-aware: consecutive
+  // workgroup ids go round-robin to the 8 XCDs, each with its own L2, so the
+  // ids are renumbered to give every XCD a contiguous run of (key head, value
+  // head, slice) -- the workgroups that read the same k, q and chunk records
+  // then share one L2.
+  const int nslice = kD / kDVS, per_seq = a.Hv * nslice, total = a.N * per_seq;
+  int lin = blockIdx.x;
+  if (total % kXcds == 0) lin = (lin % kXcds) * (total / kXcds) + lin / kXcds;
+  const int n = lin / per_seq, slice = lin % nslice, h = (lin % per_seq) / nslice;
   const int kh = h / (a.Hv / a.Hk);
   const int vcol = slice * kDVS + 16 * wave + c;  // this lane's value channel
   int bos, eos, jb;
@@ -576,117 +622,164 @@ __global__ __launch_bounds__(kNT) void chunk_rec_kernel(ChunkArgs a, const unsig
   const size_t vts = (size_t)a.Hv * kD;   // token stride of v and o
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (size_t)kh * kD;
   const uint16_t* qg = static_cast<const uint16_t*>(a.q) + (size_t)kh * kD;
-  TO* og = static_cast<TO*>(a.o) + ((size_t)(bos + 4 * q4) * a.Hv + h) * kD + vcol;
-  const int row_bytes = a.Hk * kD * 2;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + (size_t)h * kD + slice * kDVS;
+  TO* og = static_cast<TO*>(a.o) + ((size_t)(bos + c) * a.Hv + h) * kD + slice * kDVS + 16 * wave + 4 * q4;
+  const int row_bytes = (int)(kqts * 2), vrow_bytes = (int)(vts * 2);
 
-  const int vrow_bytes = a.Hv * kD * 2;
-  const uint16_t* vgb = static_cast<const uint16_t*>(a.v) + (size_t)h * kD + slice * kDVS;  // v row base
-
-  BlockSrc full[kLoadsPerWave];  // full-chunk sources of this lane's direct loads
+  RecLane ln;
+  {
+    const uint32_t s0 = (uint32_t)((lane & 15) ^ (4 * (lane >> 4)));
+    const uint32_t rb = (uint32_t)(lane >> 4) * row_bytes;
+    ln.slot0 = s0;
+    ln.kq_e = rb + 16 * (s0 ^ (uint32_t)wave);
+    ln.kq_o = rb + 16 * (s0 ^ (uint32_t)(wave + 2));
+    ln.lane16 = 16 * lane;
+    ln.fac = wave ? 16 * min(lane, 7) : 16 * lane;
+    ln.v = (uint32_t)(lane >> 2) * vrow_bytes + 16 * (lane & 3);
+  }
+  // LDS byte offsets of this lane's fragment reads (see RecBuf and the
+  // record layout).  xo[ks]: k/q row 16 ti + c (ti added as 4096 ti), key
+  // channels 32 ks + 8 q4 .. +7.  mA: T/P rows 16 ti + c < 32, columns
+  // 8 q4 .. +7; mB[ks]: rows >= 32, columns 32 ks + 8 q4 .. +7.
+  int xo[4], tro[4];
+  const int fx = kqswz(c);
 #pragma unroll
-  for (int jj = 0; jj < kLoadsPerWave; ++jj) full[jj] = block_src(wave + 4 * jj, lane, row_bytes, vrow_bytes, kC);
+  for (int ks = 0; ks < 4; ++ks) {
+    xo[ks] = 256 * c + 16 * ((4 * ks + q4) ^ fx);
+    tro[ks] = 256 * (4 * q4 + (c >> 2)) + 16 * (4 * (ks ^ (c >> 2)) + ((c & 3) ^ q4));
+  }
+  const int mA = 64 * c + 16 * (q4 ^ ((c >> 1) & 3));
+  const int mB0 = 2048 + 128 * c + 16 * (q4 ^ (c & 7));
+  const int mB1 = 2048 + 128 * c + 16 * ((4 + q4) ^ (c & 7));
+  const int vto = 64 * (4 * q4 + (c >> 2)) + 2 * (16 * wave + 4 * (c & 3));
 
-  // State S^T tiles (kd-tile kt): lane holds S[vcol][16 kt + 4 q4 + i].
+  // State S^T tiles: tile 2 ks + hh, lane holds S[vcol][32 ks + 8 q4 + 4 hh + i].
   f32x4 s[8];
-  const size_t sbase = ((size_t)n * a.Hv + h) * kD * kD + (size_t)vcol * kD + 4 * q4;
+  const size_t sbase = ((size_t)n * a.Hv + h) * kD * kD + (size_t)vcol * kD + 8 * q4;
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt)
-    s[kt] = a.initial_state ? *reinterpret_cast<const f32x4*>(a.initial_state + sbase + 16 * kt)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
+    s[kt] = a.initial_state
+                ? *reinterpret_cast<const f32x4*>(a.initial_state + sbase + 32 * (kt >> 1) + 4 * (kt & 1))
+                : f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Sources of the chunk at token cc (index jc): uniform bases + per-lane offsets.
-  const uint16_t *nk = nullptr, *nq = nullptr, *nv = nullptr;
-  const unsigned char* nr = nullptr;
-  BlockSrc nsrc[kLoadsPerWave];
-  auto prepare = [&](int cc, int jc) {
+  // Direct loads of loads jj0..jj1-1 of the chunk at token cc (index jc) into nb.
+  auto issue = [&](RecBuf* nb, int cc, int jc, int jj0, int jj1) {
     const int Lc = min(kC, eos - cc);
-    nk = kg + (size_t)cc * kqts;
-    nq = qg + (size_t)cc * kqts;
-    nv = vgb + (size_t)cc * vts;
-    nr = recs + (size_t)jc * rstride;
-    if (Lc < kC) {
-#pragma unroll
-      for (int jj = 0; jj < kLoadsPerWave; ++jj) nsrc[jj] = block_src(wave + 4 * jj, lane, row_bytes, vrow_bytes, Lc);
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < kLoadsPerWave; ++jj) nsrc[jj] = full[jj];
-    }
+    const unsigned char* nk = reinterpret_cast<const unsigned char*>(kg + (size_t)cc * kqts);
+    const unsigned char* nq = reinterpret_cast<const unsigned char*>(qg + (size_t)cc * kqts);
+    const unsigned char* nv = reinterpret_cast<const unsigned char*>(vg + (size_t)cc * vts);
+    const unsigned char* nr = recs + (size_t)jc * rstride;
+    if (Lc == kC) rec_issue<true>(nb, nk, nq, nr, nv, ln, wave, lane, row_bytes, vrow_bytes, kC, jj0, jj1);
+    else rec_issue<false>(nb, nk, nq, nr, nv, ln, wave, lane, row_bytes, vrow_bytes, Lc, jj0, jj1);
   };
-  if (bos < eos) {
-    prepare(bos, jb);
-    rec_issue_lds(bufs, nk, nq, nr, nv, nsrc, wave, 0, kLoadsPerWave);
-  }
+  if (bos < eos) issue(bufs, bos, jb, 0, kLoadsPerWave);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
+  // The transposing LDS reads come first in each iteration, while no direct
+  // load or store is in flight: the compiler waits for every outstanding
+  // vector memory operation before them.  So the state update of chunk j-1
+  // (which reads chunk j-1's k tile) opens iteration j, and the prefetch of
+  // chunk j+1 into that buffer follows a barrier.
   f32x4 Oprev[4];
+  bf16x8 dph[2], dpl[2];  // Delta' of the previous chunk, for its state update
   int pL = 0;
   int it = 0;
   for (int c0 = bos, j = jb; c0 < eos; c0 += kC, ++j, ++it) {
     const int L = min(kC, eos - c0);
     RecBuf& B = bufs[it & 1];
-    RecBuf* NB = bufs + ((it & 1) ^ 1);
+    RecBuf* NB = bufs + ((it & 1) ^ 1);  // chunk j-1's inputs, then chunk j+1's
+    const unsigned char* bb = reinterpret_cast<const unsigned char*>(&B);
     const bool more = c0 + kC < eos;
-    if (more) prepare(c0 + kC, j + 1);
+    if (it > 0) state_update(s, *NB, dph, dpl, tro);
+    // v[16 ti + 4 q4 + e][vcol], e = 0..3, one transposing read per tile
+    v4i16 vt[4];
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+      vt[ti] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_ptr)(reinterpret_cast<const unsigned char*>(&B.V[0][0]) + vto + 1024 * ti));
+    __syncthreads();  // every wave is done with chunk j-1's buffer
     TO* oprev = og + (size_t)(c0 - kC - bos) * vts;
-    if (more) rec_issue_lds(NB, nk, nq, nr, nv, nsrc, wave, 0, 5);
-    if (it > 0) store_out(oprev, vts, Oprev, pL, q4, 0, 1);
 
     // ---- state phase: this wave's 16 value channels
     bf16x8 sbh[4], sbl[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) split8(s[2 * ks], s[2 * ks + 1], sbh[ks], sbl[ks]);
 
+    // X = K S0^T (tokens x channels) and Y^T = S0 Q^T (channels x tokens);
+    // the k and q fragments of tile ti + 1 are read while tile ti multiplies
+    auto rd_kq = [&](int ti, bf16x8* fk, bf16x8* fq) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        fk[ks] = lds8(reinterpret_cast<const uint16_t*>(bb + offsetof(RecBuf, K) + xo[ks] + 4096 * ti));
+        fq[ks] = lds8(reinterpret_cast<const uint16_t*>(bb + offsetof(RecBuf, Q) + xo[ks] + 4096 * ti));
+      }
+    };
+    bf16x8 fk[2][4], fq[2][4];
+    rd_kq(0, fk[0], fq[0]);
     f32x4 R[4], Y[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
+      if (ti < 3) rd_kq(ti + 1, fk[(ti + 1) & 1], fq[(ti + 1) & 1]);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint16_t* kr = &B.Kr[16 * ti + c][32 * ks + 4 * q4];
-        const uint16_t* qr = &B.Qr[16 * ti + c][32 * ks + 4 * q4];
-        const u32x2 k0 = *reinterpret_cast<const u32x2*>(kr), k1 = *reinterpret_cast<const u32x2*>(kr + 16);
-        const u32x2 q0 = *reinterpret_cast<const u32x2*>(qr), q1 = *reinterpret_cast<const u32x2*>(qr + 16);
-        const bf16x8 ak = __builtin_bit_cast(bf16x8, u32x4{k0[0], k0[1], k1[0], k1[1]});
-        const bf16x8 aq = __builtin_bit_cast(bf16x8, u32x4{q0[0], q0[1], q1[0], q1[1]});
+        const bf16x8 ak = fk[ti & 1][ks], aq = fq[ti & 1][ks];
         acc = mfma16x16x32(ak, sbh[ks], acc);
-        y = mfma16x16x32(aq, sbh[ks], y);
+        y = mfma16x16x32(sbh[ks], aq, y);
         acc = mfma16x16x32(ak, sbl[ks], acc);
-        y = mfma16x16x32(aq, sbl[ks], y);
+        y = mfma16x16x32(sbl[ks], aq, y);
       }
-      // v[16 ti + 4 q4 + e][vcol], e = 0..3, by one transposing read
-      const v4i16 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4i16_ptr)(&B.V[16 * ti + 4 * q4 + (c >> 2)][16 * wave + 4 * (c & 3)]));
+      // prefetch of the next chunk and stores of the previous chunk's
+      // outputs, spread over the state phase
+      if (more) issue(NB, c0 + kC, j + 1, 8 * ti, min(8 * ti + 8, kLoadsPerWave));
+      if (it > 0 && (ti & 1)) store_out(oprev, vts, Oprev, pL, c, ti - 1, ti + 1);
       const f32x4 btv = *reinterpret_cast<const f32x4*>(&B.fac[0][16 * ti + 4 * q4]);
       const f32x4 xrv = *reinterpret_cast<const f32x4*>(&B.fac[1][16 * ti + 4 * q4]);
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4)
-        R[ti][i4] = btv[i4] * __uint_as_float((uint32_t)(uint16_t)vt[i4] << 16) - xrv[i4] * acc[i4];
-      Y[ti] = y * *reinterpret_cast<const f32x4*>(&B.fac[2][16 * ti + 4 * q4]);
+        R[ti][i4] = btv[i4] * __uint_as_float((uint32_t)(uint16_t)vt[ti][i4] << 16) - xrv[i4] * acc[i4];
+      Y[ti] = y * B.fac[2][16 * ti + c];  // Y^T: token 16 ti + c
     }
-    if (more) rec_issue_lds(NB, nk, nq, nr, nv, nsrc, wave, 5, 10);
-    if (it > 0) store_out(oprev, vts, Oprev, pL, q4, 1, 2);
 
     bf16x8 rbh[2], rbl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) split8(R[2 * ks], R[2 * ks + 1], rbh[ks], rbl[ks]);
 
+    // Delta = T R; T is block lower triangular, so 32-wide steps above the
+    // diagonal are skipped
+    auto mrd = [&](int m, int ti, int ks) {
+      const int o = ti < 2 ? mA + 1024 * ti : (ks ? mB1 : mB0) + 2048 * (ti - 2);
+      return lds8(reinterpret_cast<const uint16_t*>(bb + offsetof(RecBuf, M) + m * kMatBytes + o));
+    };
+    // the six nonzero 32-wide steps (ti, ks) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+    bf16x8 th[6], tl[6], ph[6], pl[6];
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int ti = u < 2 ? u : 2 + (u - 2) / 2, ks = u < 2 ? 0 : (u - 2) % 2;
+      th[u] = mrd(0, ti, ks);
+      tl[u] = mrd(1, ti, ks);
+    }
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int ti = u < 2 ? u : 2 + (u - 2) / 2, ks = u < 2 ? 0 : (u - 2) % 2;
+      ph[u] = mrd(2, ti, ks);
+      pl[u] = mrd(3, ti, ks);
+    }
     f32x4 Dl[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const int ro = mrow(16 * ti + c);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         if (2 * ks > ti) continue;
-        const int off = ro + 2 * (32 * ks + 8 * q4);
-        acc = mfma3(lds8(reinterpret_cast<const uint16_t*>(&B.M[0][off])),
-                    lds8(reinterpret_cast<const uint16_t*>(&B.M[1][off])), rbh[ks], rbl[ks], acc);
+        const int u = ti < 2 ? ti : 2 + 2 * (ti - 2) + ks;
+        acc = mfma3(th[u], tl[u], rbh[ks], rbl[ks], acc);
       }
       Dl[ti] = acc;
     }
-    bf16x8 dbh[2], dbl[2], dph[2], dpl[2];
+    bf16x8 dbh[2], dbl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       split8(Dl[2 * ks], Dl[2 * ks + 1], dbh[ks], dbl[ks]);
@@ -694,61 +787,44 @@ __global__ __launch_bounds__(kNT) void chunk_rec_kernel(ChunkArgs a, const unsig
       const f32x4 cl1 = *reinterpret_cast<const f32x4*>(&B.fac[3][32 * ks + 16 + 4 * q4]);
       split8(Dl[2 * ks] * cl0, Dl[2 * ks + 1] * cl1, dph[ks], dpl[ks]);
     }
-    if (more) rec_issue_lds(NB, nk, nq, nr, nv, nsrc, wave, 10, 15);
-    if (it > 0) store_out(oprev, vts, Oprev, pL, q4, 2, 4);
 
-    // outputs O = yq * (Q S0^T) + P Delta (stored during the next chunk)
+    // outputs, transposed: O^T = yq * (S0 Q^T) + Delta^T P^T (stored during
+    // the next chunk)
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
       f32x4 y = Y[ti];
-      const int ro = mrow(16 * ti + c);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         if (2 * ks > ti) continue;
-        const int off = ro + 2 * (32 * ks + 8 * q4);
-        y = mfma3(lds8(reinterpret_cast<const uint16_t*>(&B.M[2][off])),
-                  lds8(reinterpret_cast<const uint16_t*>(&B.M[3][off])), dbh[ks], dbl[ks], y);
+        const int u = ti < 2 ? ti : 2 + 2 * (ti - 2) + ks;
+        y = mfma3(dbh[ks], dbl[ks], ph[u], pl[u], y);
       }
       Oprev[ti] = y;
-    }
-    if (more) rec_issue_lds(NB, nk, nq, nr, nv, nsrc, wave, 15, kLoadsPerWave);
-
-    // state update S^T <- e^{G_L} S^T + K^T Delta'; K^T fragments by
-    // transposing reads of the row-major k tile (last: the compiler waits for
-    // the prefetch before these reads)
-    const float eGL = B.eGL[0];
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
-      f32x4 acc = s[kt] * eGL;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int r0 = 32 * ks + 4 * q4 + (c >> 2), col = 16 * kt + 4 * (c & 3);
-        const bf16x8 akt = tr_frag(&B.Kr[r0][col], &B.Kr[r0 + 16][col]);
-        acc = mfma16x16x32(akt, dph[ks], acc);
-        acc = mfma16x16x32(akt, dpl[ks], acc);
-      }
-      s[kt] = acc;
     }
     pL = L;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  if (it > 0) store_out(og + (size_t)(eos - pL - bos) * vts, vts, Oprev, pL, q4, 0, 4);
+  if (it > 0) {
+    state_update(s, bufs[(it - 1) & 1], dph, dpl, tro);
+    store_out(og + (size_t)(eos - pL - bos) * vts, vts, Oprev, pL, c, 0, 4);
+  }
 
   if (a.final_state) {
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) *reinterpret_cast<f32x4*>(a.final_state + sbase + 16 * kt) = s[kt];
+    for (int kt = 0; kt < 8; ++kt)
+      *reinterpret_cast<f32x4*>(a.final_state + sbase + 32 * (kt >> 1) + 4 * (kt & 1)) = s[kt];
   }
 }
 
 template <typename TO>
 hipError_t launch_rec_t(const ChunkArgs& a, const unsigned char* ws, hipStream_t st) {
   auto kern = chunk_rec_kernel<TO>;
-  const size_t smem = 2 * sizeof(RecBuf);  // 148 KiB: double-buffered chunk inputs
+  const size_t smem = 2 * sizeof(RecBuf);  // 124 KiB: double-buffered chunk inputs
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(kD / kDVS, a.Hv, a.N), dim3(kNT), smem, st, a, ws);
+  hipLaunchKernelGGL(kern, dim3((kD / kDVS) * a.Hv * a.N), dim3(kRecNT), smem, st, a, ws);
   return hipGetLastError();
 }
 
