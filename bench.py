@@ -12,9 +12,13 @@ reports, measured in the same run:
                step, state updated in place, 256 steps: state GB/s
   pipeline  -- the whole layer path over a packed batch of 8 sequences
                (65536 tokens): conv+SiLU+gates, recurrence, gated RMSNorm
-  roofline  -- the prefill kernel's algorithmic HBM bytes per launch divided
-               by its average launch time (HIP events on the launch stream),
-               against the 8 TB/s HBM peak, plus its MFMA fraction
+  roofline  -- the dominant kernel of the call, the state-carrying
+               recurrence (gdr_chunk_fwd_recurrence): its algorithmic HBM bytes
+               per launch (q, k, v read, o written, state in and out) over its
+               average launch time (HIP events on the launch stream, around
+               each recurrence launch inside the timed loop), against the
+               8 TB/s HBM peak; plus its MFMA fraction and the HBM bytes the
+               committed rocprofv3 counters measured for it
   cpu_baseline -- the fp64 CPU oracle timed on the host cores on a bounded
                sample (4096 tokens of the same layer)
 
@@ -48,6 +52,13 @@ STATE_BYTES = HV * D * D * 4
 # Algorithmic FLOPs per token of the chunk form (triangle-exact):
 # Hv*(6*dk*dv + 2*C*dv + C^2/3) + Hk*2*C*dk
 PREFILL_FLOP_PER_TOKEN = HV * (6 * D * D + 2 * C * D + C * C / 3) + HK * 2 * C * D
+# The recurrence kernel's share: q, k, v read and o written per token (g and
+# beta are read by the prepare stage), and the state-dependent products
+# X = K S0^T, Y = Q S0^T, the state update (2 dk dv each) and T R, P Delta
+# (C dv each, triangle-exact).
+RECUR_BYTES_PER_TOKEN = 2 * HK * D * 2 + HV * D * 2 + HV * D * 4
+RECUR_FLOP_PER_TOKEN = HV * (6 * D * D + 2 * C * D)
+RECUR_KERNEL = "gdr::chunk_rec_kernel<float>"
 COUNTERS = os.path.join(ROOT, "profiles", "chunk_prefill_T32768_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_amd", "csrc", "kernels", "chunk_bf16.hip")
 
@@ -74,32 +85,40 @@ def bench_prefill(steps: int, warmup: int):
     g, beta = f32(x.g), f32(x.beta)
     state = torch.zeros((1, HV, D, D), device=dev)
     o = torch.empty((1, T_CALL, HV, D), device=dev)
+    ws = gdr.chunk_workspace(q, v)
     del x
 
-    def step():
-        gdr.chunk_gated_delta_rule(q, k, v, g, beta, state, final_state=state, out=o)
+    # One call = gdr_chunk_fwd_prepare + gdr_chunk_fwd_recurrence on the torch
+    # stream (the same kernels gdr_chunk_fwd enqueues), so that events can
+    # bracket the recurrence kernel alone.
+    def stage(name):
+        gdr.chunk_gated_delta_rule(q, k, v, g, beta, state, final_state=state, out=o, workspace=ws, stage=name)
 
     log(f"prefill: {warmup} warmup + {steps} timed 32K calls")
     for _ in range(warmup):
-        step()
+        stage("prepare")
+        stage("recurrence")
     torch.cuda.synchronize()
     per = []
     t0 = time.perf_counter()
     start, end = _events()
     start.record()
     for _ in range(steps):
-        e0, e1 = _events()
-        e0.record()
-        step()
-        e1.record()
-        per.append((e0, e1))
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        stage("prepare")
+        e[1].record()
+        stage("recurrence")
+        e[2].record()
+        per.append(e)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    launch_ms = [a.elapsed_time(b) for a, b in per]
+    prep_ms = [e[0].elapsed_time(e[1]) for e in per]
+    recur_ms = [e[1].elapsed_time(e[2]) for e in per]
     finite = bool(torch.isfinite(state).all() and torch.isfinite(o).all())
-    return dict(total_ms=total_ms, wall_s=wall, launch_ms=launch_ms, finite=finite)
+    return dict(total_ms=total_ms, wall_s=wall, prep_ms=prep_ms, recur_ms=recur_ms, finite=finite)
 
 
 def bench_decode(steps: int = 256, replicas: int = 1):
@@ -223,7 +242,7 @@ def traffic_from_counters():
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=16)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "pipeline", "copy"])
     ap.add_argument("--no-cpu", action="store_true")
@@ -243,9 +262,10 @@ def main():
     if args.only in ("all", "prefill"):
         pf = bench_prefill(args.steps, args.warmup)
         ms_step = pf["total_ms"] / args.steps
-        avg_launch_ms = float(np.mean(pf["launch_ms"]))
-        bytes_launch = T_CALL * PREFILL_BYTES_PER_TOKEN + 2 * STATE_BYTES
+        avg_launch_ms = float(np.mean(pf["recur_ms"]))
+        bytes_launch = T_CALL * RECUR_BYTES_PER_TOKEN + 2 * STATE_BYTES
         achieved = bytes_launch / (avg_launch_ms * 1e-3) / 1e9
+        call_bytes = T_CALL * PREFILL_BYTES_PER_TOKEN + 2 * STATE_BYTES
         traffic, tstat = traffic_from_counters()
         tok_s = T_CALL * args.steps / (pf["total_ms"] * 1e-3)
         out.update({
@@ -266,10 +286,13 @@ def main():
                        "chunk": C, "qkv": "bf16", "gates_state_out": "fp32", "parallelism": "single GPU"},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                         "kernel": "chunk_bf16_kernel", "avg_launch_ms": avg_launch_ms,
+                         "kernel": RECUR_KERNEL, "avg_launch_ms": avg_launch_ms,
                          "algorithmic_bytes_per_launch": bytes_launch,
-                         "mfma_frac": PREFILL_FLOP_PER_TOKEN * T_CALL / (avg_launch_ms * 1e-3) / 1e12
+                         "mfma_frac": RECUR_FLOP_PER_TOKEN * T_CALL / (avg_launch_ms * 1e-3) / 1e12
                          / BF16_PEAK_TFLOPS},
+            "call": {"prepare_ms": float(np.mean(pf["prep_ms"])), "recurrence_ms": avg_launch_ms,
+                     "hbm_frac": call_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "mfma_frac": PREFILL_FLOP_PER_TOKEN * T_CALL / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
             "finite": pf["finite"],
         })
         if tstat == "stale":

@@ -7,6 +7,7 @@ if it has not been built (``python -m gated_delta_rule_amd.build``).
 from ._lib import GDRError, load as load_library  # noqa: F401
 from .ops import (  # noqa: F401
     chunk_gated_delta_rule,
+    chunk_workspace,
     conv_gate_fused,
     gated_rmsnorm,
     recurrent_step,
@@ -16,6 +17,7 @@ __all__ = [
     "GDRError",
     "load_library",
     "chunk_gated_delta_rule",
+    "chunk_workspace",
     "recurrent_step",
     "conv_gate_fused",
     "gated_rmsnorm",

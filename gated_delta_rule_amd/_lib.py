@@ -20,6 +20,8 @@ EXPORTED = (
     "gdr_last_error",
     "gdr_chunk_fwd_workspace_size",
     "gdr_chunk_fwd",
+    "gdr_chunk_fwd_prepare",
+    "gdr_chunk_fwd_recurrence",
     "gdr_recurrent_step",
     "gdr_conv_gate_fused",
     "gdr_gated_rmsnorm",
@@ -97,8 +99,10 @@ def load() -> ctypes.CDLL:
     lib.gdr_last_error.argtypes = []
     lib.gdr_chunk_fwd_workspace_size.restype = I32
     lib.gdr_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(GdrDesc), ctypes.POINTER(SZ)]
-    lib.gdr_chunk_fwd.restype = I32
-    lib.gdr_chunk_fwd.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]
+    for name in ("gdr_chunk_fwd", "gdr_chunk_fwd_prepare", "gdr_chunk_fwd_recurrence"):
+        fn = getattr(lib, name)
+        fn.restype = I32
+        fn.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.gdr_recurrent_step.restype = I32
     lib.gdr_recurrent_step.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, P, P]
     lib.gdr_conv_gate_fused.restype = I32

@@ -125,10 +125,11 @@ gdr_status gdr_chunk_fwd_workspace_size(const gdr_desc* d, size_t* bytes) {
   return ok();
 }
 
-gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
-                         const float* beta, const float* initial_state, float* final_state,
-                         const int32_t* cu_seqlens, void* o, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+// gdr_chunk_fwd and its two stages: checks, then the stages asked for.
+static gdr_status chunk_fwd(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                            const float* beta, const float* initial_state, float* final_state,
+                            const int32_t* cu_seqlens, void* o, void* workspace, size_t workspace_bytes,
+                            void* stream, int stages, const char* name) {
   gdr_status st = check_desc(d, false, cu_seqlens != nullptr);
   if (st != GDR_OK) return st;
   const long long tokens = (long long)d->batch * d->seq_len;
@@ -165,8 +166,34 @@ gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const 
   a.scale = d->scale;
   a.eps = d->l2norm_eps;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(mfma_path(d) ? gdr::launch_chunk_bf16(a, workspace, s) : gdr::launch_chunk_f32(a, s),
-                    "gdr_chunk_fwd launch");
+  if (mfma_path(d)) return hip_status(gdr::launch_chunk_bf16(a, workspace, s, stages), name);
+  // the fp32 path has no prepare stage: the recurrence stage does all the work
+  if (!(stages & gdr::kStageRecur)) return ok();
+  return hip_status(gdr::launch_chunk_f32(a, s), name);
+}
+
+gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                         const float* beta, const float* initial_state, float* final_state,
+                         const int32_t* cu_seqlens, void* o, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return chunk_fwd(d, q, k, v, g, beta, initial_state, final_state, cu_seqlens, o, workspace, workspace_bytes,
+                   stream, gdr::kStagePrepare | gdr::kStageRecur, "gdr_chunk_fwd launch");
+}
+
+gdr_status gdr_chunk_fwd_prepare(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* initial_state, float* final_state,
+                                 const int32_t* cu_seqlens, void* o, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return chunk_fwd(d, q, k, v, g, beta, initial_state, final_state, cu_seqlens, o, workspace, workspace_bytes,
+                   stream, gdr::kStagePrepare, "gdr_chunk_fwd_prepare launch");
+}
+
+gdr_status gdr_chunk_fwd_recurrence(const gdr_desc* d, const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta, const float* initial_state,
+                                    float* final_state, const int32_t* cu_seqlens, void* o, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  return chunk_fwd(d, q, k, v, g, beta, initial_state, final_state, cu_seqlens, o, workspace, workspace_bytes,
+                   stream, gdr::kStageRecur, "gdr_chunk_fwd_recurrence launch");
 }
 
 gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,

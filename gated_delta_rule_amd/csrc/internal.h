@@ -54,9 +54,12 @@ struct NormArgs {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t st);
 // The bf16-MFMA prefill needs a device workspace of
-// chunk_bf16_workspace_bytes(a) bytes (chunk table + per-chunk records).
+// chunk_bf16_workspace_bytes(a) bytes (chunk table + per-chunk records).  It
+// runs in two stages: kStagePrepare fills the workspace (state-independent
+// per-chunk factors), kStageRecur carries the state through the chunks.
+constexpr int kStagePrepare = 1, kStageRecur = 2;
 size_t chunk_bf16_workspace_bytes(const ChunkArgs& a);
-hipError_t launch_chunk_bf16(const ChunkArgs& a, void* workspace, hipStream_t st);
+hipError_t launch_chunk_bf16(const ChunkArgs& a, void* workspace, hipStream_t st, int stages);
 hipError_t launch_conv_front(const ConvArgs& a, hipStream_t st);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t st);
 

@@ -839,8 +839,9 @@ size_t chunk_bf16_workspace_bytes(const ChunkArgs& a) {
   return kTableBytes(a.N) + max_chunks(a) * (size_t)a.Hv * kRecBytes;
 }
 
-hipError_t launch_chunk_bf16(const ChunkArgs& a, void* workspace, hipStream_t st) {
+hipError_t launch_chunk_bf16(const ChunkArgs& a, void* workspace, hipStream_t st, int stages) {
   unsigned char* ws = static_cast<unsigned char*>(workspace);
+  if (!(stages & kStagePrepare)) return a.out_bf16 ? launch_rec_t<uint16_t>(a, ws, st) : launch_rec_t<float>(a, ws, st);
   if (a.cu_seqlens) {
     hipLaunchKernelGGL(chunk_table_kernel, dim3(1), dim3(1024), 0, st, a.cu_seqlens, a.N,
                        reinterpret_cast<int32_t*>(ws));
@@ -857,6 +858,7 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, void* workspace, hipStream_t st
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (!(stages & kStageRecur)) return hipSuccess;
   return a.out_bf16 ? launch_rec_t<uint16_t>(a, ws, st) : launch_rec_t<float>(a, ws, st);
 }
 

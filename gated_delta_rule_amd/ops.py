@@ -57,7 +57,8 @@ def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
                            chunk_size: int = 64, out_dtype: torch.dtype = torch.float32,
                            final_state: Optional[torch.Tensor] = None,
                            out: Optional[torch.Tensor] = None,
-                           workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                           workspace: Optional[torch.Tensor] = None,
+                           stage: str = "all") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked prefill (gdr_chunk_fwd).
 
     q, k: [B, T, Hk, d]; v: [B, T, Hv, d] (bf16 or fp32, same dtype);
@@ -65,8 +66,15 @@ def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
     cu_seqlens: int32 [N+1] (then B must be 1).  ``final_state`` may be given
     as a preallocated output (it may be ``initial_state`` itself); ``workspace``
     (uint8, device) is used if large enough, else one is allocated.
+    ``stage``: "all" (gdr_chunk_fwd), or "prepare" / "recurrence" for the two
+    stages alone (gdr_chunk_fwd_prepare / gdr_chunk_fwd_recurrence; pass the
+    same ``workspace``, ``out`` and ``final_state`` to both).
     Returns (o [B, T, Hv, d] out_dtype, final_state or None).
     """
+    entry = {"all": "gdr_chunk_fwd", "prepare": "gdr_chunk_fwd_prepare",
+             "recurrence": "gdr_chunk_fwd_recurrence"}.get(stage)
+    if entry is None:
+        raise ValueError(f"unknown stage {stage!r}")
     dev = q.device
     qd = q.dtype
     for t, name in ((q, "q"), (k, "k"), (v, "v")):
@@ -106,12 +114,27 @@ def chunk_gated_delta_rule(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g:
     _lib.check("gdr_chunk_fwd_workspace_size", lib.gdr_chunk_fwd_workspace_size(ctypes.byref(desc),
                                                                                 ctypes.byref(nbytes)))
     if workspace is None or workspace.numel() < nbytes.value:
+        if stage != "all" and nbytes.value:
+            raise ValueError(f"stage {stage!r} needs a workspace of {nbytes.value} bytes")
         workspace = torch.empty(nbytes.value, device=dev, dtype=torch.uint8) if nbytes.value else None
-    st = lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                           _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(out),
-                           _ptr(workspace), nbytes.value, _stream(dev))
-    _lib.check("gdr_chunk_fwd", st)
+    st = getattr(lib, entry)(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), _ptr(out),
+                             _ptr(workspace), nbytes.value, _stream(dev))
+    _lib.check(entry, st)
     return out, final_state
+
+
+def chunk_workspace(q: torch.Tensor, v: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                    chunk_size: int = 64, out_dtype: torch.dtype = torch.float32) -> Optional[torch.Tensor]:
+    """A device workspace (uint8) of the size gdr_chunk_fwd needs for these
+    shapes (gdr_chunk_fwd_workspace_size), or None if it needs none."""
+    B, T, Hk, D = q.shape
+    N = cu_seqlens.numel() - 1 if cu_seqlens is not None else B
+    desc = make_desc(B, T, N, Hk, v.shape[2], D, chunk_size, q.dtype, out_dtype, True, 1.0, 1e-6)
+    nbytes = ctypes.c_size_t(0)
+    _lib.check("gdr_chunk_fwd_workspace_size",
+               _lib.load().gdr_chunk_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(nbytes)))
+    return torch.empty(nbytes.value, device=q.device, dtype=torch.uint8) if nbytes.value else None
 
 
 def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,

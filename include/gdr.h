@@ -142,6 +142,29 @@ gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const 
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The two stages of gdr_chunk_fwd, for callers that time or schedule them
+ * apart.  Arguments, checks and errors are those of gdr_chunk_fwd, and
+ * gdr_chunk_fwd_prepare followed by gdr_chunk_fwd_recurrence on one stream
+ * with the same arguments and workspace is gdr_chunk_fwd, bit for bit.
+ *   prepare:    fills the workspace with everything that does not depend on
+ *               the state (per-chunk decays, q/k norms, (I+A)^{-1} and the
+ *               causal decayed q.k products); writes nothing else
+ *   recurrence: carries the state through the chunks using that workspace;
+ *               writes o and final_state.  The workspace must not change
+ *               between the two calls.
+ * On a combination whose workspace size is 0, prepare enqueues nothing and
+ * recurrence does all the work.
+ */
+gdr_status gdr_chunk_fwd_prepare(const gdr_desc* d, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* initial_state,
+                                 float* final_state, const int32_t* cu_seqlens, void* o,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+gdr_status gdr_chunk_fwd_recurrence(const gdr_desc* d, const void* q, const void* k, const void* v,
+                                    const float* g, const float* beta, const float* initial_state,
+                                    float* final_state, const int32_t* cu_seqlens, void* o,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode token for N independent sequences (the pages' single-step
  * fused recurrent path).  d->batch = N, d->seq_len = 1, cu_seqlens unused.
  *

@@ -55,10 +55,13 @@ def _desc(**kw):
 FAKE = 0x7F0000000000  # never dereferenced: every case below fails validation first
 
 
-def _chunk(d, q=FAKE, cu=None, o=FAKE, init=None, fin=None):
+CHUNK_ENTRIES = ("gdr_chunk_fwd", "gdr_chunk_fwd_prepare", "gdr_chunk_fwd_recurrence")
+
+
+def _chunk(d, q=FAKE, cu=None, o=FAKE, init=None, fin=None, entry="gdr_chunk_fwd"):
     lib = _lib.load()
-    return lib.gdr_chunk_fwd(ctypes.byref(d) if d is not None else None, q, FAKE, FAKE, FAKE, FAKE, init, fin,
-                             cu, o, None, 0, None)
+    return getattr(lib, entry)(ctypes.byref(d) if d is not None else None, q, FAKE, FAKE, FAKE, FAKE, init, fin,
+                               cu, o, None, 0, None)
 
 
 @pytest.mark.parametrize("kw,status,msg", [
@@ -73,18 +76,22 @@ def _chunk(d, q=FAKE, cu=None, o=FAKE, init=None, fin=None):
     (dict(l2norm_eps=-1.0), -1, "eps"),
     (dict(struct_size=8), -1, "struct_size"),
 ])
-def test_chunk_fwd_rejects_bad_descriptors(kw, status, msg):
-    assert _chunk(_desc(**kw)) == status
+@pytest.mark.parametrize("entry", CHUNK_ENTRIES)
+def test_chunk_fwd_rejects_bad_descriptors(kw, status, msg, entry):
+    assert _chunk(_desc(**kw), entry=entry) == status
     assert msg in _lib.load().gdr_last_error().decode()
 
 
-def test_chunk_fwd_rejects_null_and_misaligned():
+@pytest.mark.parametrize("entry", CHUNK_ENTRIES)
+def test_chunk_fwd_rejects_null_and_misaligned(entry):
     lib = _lib.load()
-    assert _chunk(None) == -1
-    assert _chunk(_desc(), q=None) == -1 and "required" in lib.gdr_last_error().decode()
-    assert _chunk(_desc(), q=FAKE + 2) == -1 and "aligned" in lib.gdr_last_error().decode()
-    assert _chunk(_desc(), fin=FAKE + 4) == -1
-    assert _chunk(_desc(batch=2, num_seqs=2), cu=FAKE) == -1  # packed batch needs batch == 1
+    assert _chunk(None, entry=entry) == -1
+    assert _chunk(_desc(), q=None, entry=entry) == -1 and "required" in lib.gdr_last_error().decode()
+    assert _chunk(_desc(), q=FAKE + 2, entry=entry) == -1 and "aligned" in lib.gdr_last_error().decode()
+    assert _chunk(_desc(), fin=FAKE + 4, entry=entry) == -1
+    assert _chunk(_desc(batch=2, num_seqs=2), cu=FAKE, entry=entry) == -1  # packed batch needs batch == 1
+    # a bf16 d=128 call needs the workspace in either stage
+    assert _chunk(_desc(), entry=entry) == -1 and "workspace" in lib.gdr_last_error().decode()
 
 
 def test_workspace_size():

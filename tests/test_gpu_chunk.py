@@ -131,6 +131,32 @@ def test_deterministic():
     assert bits_equal(o1, o2) and bits_equal(s1, s2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_two_stages_equal_one_call_bit_exact(dtype):
+    """gdr_chunk_fwd_prepare then gdr_chunk_fwd_recurrence = gdr_chunk_fwd, bit for bit,
+    on a packed batch with a ragged tail (both the bf16-MFMA and the fp32 path)."""
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    lens = [70, 0, 129]
+    x = synth.gdr_inputs(41, B=1, T=sum(lens), dtype=dtype)
+    cu = synth.cu_seqlens_of(lens)
+    s0 = (0.05 * np.random.default_rng(42).standard_normal((len(lens), 48, 128, 128))).astype(np.float32)
+    say(f"chunk two stages vs one call, {dtype}, lengths {lens}")
+    a = _dev_inputs(x, dev, cu, s0)
+    args = (a["q"], a["k"], a["v"], a["g"], a["beta"], a["initial_state"])
+    o1, s1 = gdr_amd.chunk_gated_delta_rule(*args, output_final_state=True, cu_seqlens=a["cu_seqlens"])
+    ws = gdr_amd.chunk_workspace(a["q"], a["v"], a["cu_seqlens"])
+    assert (ws is None) == (dtype == "f32")
+    o2 = torch.empty_like(o1)
+    s2 = torch.empty_like(s1)
+    for stage in ("prepare", "recurrence"):
+        gdr_amd.chunk_gated_delta_rule(*args, cu_seqlens=a["cu_seqlens"], final_state=s2, out=o2, workspace=ws,
+                                       stage=stage)
+    torch.cuda.synchronize()
+    assert bits_equal(o1, o2) and bits_equal(s1, s2)
+
+
 @pytest.mark.parametrize("d,dtype,C", [(64, "bf16", 64), (64, "f32", 64), (128, "f32", 64), (128, "bf16", 32),
                                        (32, "bf16", 32)])
 def test_other_shapes_fp32_path(d, dtype, C):
