@@ -20,7 +20,7 @@ reports, measured in the same run:
                8 TB/s HBM peak; plus its MFMA fraction and the HBM bytes the
                committed rocprofv3 counters measured for it
   cpu_baseline -- the fp64 CPU oracle timed on the host cores on a bounded
-               sample (4096 tokens of the same layer)
+               sample of the same workload (the first three 32K-token calls)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|decode|pipeline|copy|all]
                        [--no-cpu]
@@ -213,18 +213,26 @@ def bench_copy(n_bytes: int = 1 << 30, reps: int = 5):
     return dict(bytes_each_way=n_bytes, ms=ms, GBps=2 * n_bytes / (ms * 1e-3) / 1e9)
 
 
-def cpu_baseline(T: int = 4096):
+def cpu_baseline(calls: int = 3):
+    """The fp64 oracle on the first ``calls`` 32K-token calls of the same
+    long-context workload (state carried from call to call), heads spread over
+    the host's cores.  Input generation is not timed."""
     from gated_delta_rule_amd import synth
     from oracle import gdr as ref
-    x = synth.layer_prefill(T=T)
     procs = len(os.sched_getaffinity(0))
-    log(f"cpu baseline: fp64 oracle, T={T}, 48 heads, {procs} processes")
-    t0 = time.perf_counter()
-    _, _, used = ref.forward_parallel(x.q, x.k, x.v, x.g, x.beta, processes=procs)
-    dt = time.perf_counter() - t0
-    return dict(value=T / dt, unit="tokens/s", cores=used, kind="oracle",
-                sample=f"fp64 token-serial oracle, one {T}-token prefill of the 16/48-head d=128 layer "
-                       f"(heads spread over {used} processes), {dt:.1f} s wall")
+    log(f"cpu baseline: fp64 oracle, {calls} x {T_CALL} tokens, 48 heads, {procs} processes")
+    state, dt, used = None, 0.0, procs
+    for i in range(calls):
+        x = synth.long_context_call(i, T=T_CALL)
+        t0 = time.perf_counter()
+        _, state, used = ref.forward_parallel(x.q, x.k, x.v, x.g, x.beta, state, processes=procs)
+        dt += time.perf_counter() - t0
+        del x
+    tokens = calls * T_CALL
+    return dict(value=tokens / dt, unit="tokens/s", cores=used, kind="oracle",
+                sample=f"fp64 token-serial oracle on the first {calls} 32768-token calls of the same "
+                       f"16/48-head d=128 long-context workload, state carried between calls, heads spread "
+                       f"over {used} processes: {tokens} tokens in {dt:.1f} s wall")
 
 
 def traffic_from_counters():
