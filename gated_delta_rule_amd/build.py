@@ -32,10 +32,12 @@ SOURCES = [
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 
 # Packed fp32 instructions stay off: hipcc would otherwise form v_pk_*_f32
-# from ordinary float code.
+# from ordinary float code.  Matrix-core results go to ordinary VGPRs (not the
+# accumulation registers), so the VALU work on them needs no copies.
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]

@@ -43,6 +43,7 @@ constexpr int kD = 128;  // head dim (d_k = d_v)
 constexpr int kC = 64;   // chunk
 constexpr int kNT = 256;  // threads per workgroup (4 waves)
 constexpr int kDVS = 32;  // value channels per recurrence workgroup
+constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 
 // Workspace record of one (chunk, value head), in bytes: T hi, T lo, P hi,
 // P lo (each: rows 0..31 x 32 columns, then rows 32..63 x 64 columns, bf16,
@@ -218,7 +219,13 @@ __global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigne
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int c = lane & 15, q4 = lane >> 4;
-  const int j = blockIdx.x, h = blockIdx.y;
+  // Workgroup -> (chunk j, value head h), heads fastest and XCD-aware (see
+  // chunk_rec_kernel): the three value heads of a key head run side by side
+  // on one XCD, so two of them read the chunk's k and q from its L2.
+  const int total = (int)gridDim.x;
+  int lin = blockIdx.x;
+  if (total % kXcds == 0) lin = (lin % kXcds) * (total / kXcds) + lin / kXcds;
+  const int j = lin / a.Hv, h = lin % a.Hv;
   const int32_t* table = reinterpret_cast<const int32_t*>(ws);
   const ChunkPos pos = locate_chunk(a, table, j);
   if (!pos.valid) return;
@@ -237,14 +244,20 @@ __global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigne
     uint16_t(*X)[kD + 8] = tid < 128 ? sm.Kr : sm.Qr;
     const int b = tid & 127, rb = b >> 4, cb = b & 15;
     const int pc = perm8(cb);
+    // all eight loads in flight before the LDS stores; rows past L read row
+    // L-1 (in bounds) and are zeroed
+    u32x4 w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = min(8 * rb + i, L - 1);
+      w[i] = *reinterpret_cast<const u32x4*>(src + ((size_t)(c0 + row) * a.Hk + kh) * kD + 8 * cb);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = 8 * rb + i;
-      u16x8 val = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (row < L) val = *reinterpret_cast<const u16x8*>(src + ((size_t)(c0 + row) * a.Hk + kh) * kD + 8 * cb);
-      const u32x4 w = __builtin_bit_cast(u32x4, val);
-      *reinterpret_cast<u32x2*>(&X[row][pc]) = u32x2{w[0], w[1]};
-      *reinterpret_cast<u32x2*>(&X[row][pc + 8]) = u32x2{w[2], w[3]};
+      const u32x4 v = row < L ? w[i] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x2*>(&X[row][pc]) = u32x2{v[0], v[1]};
+      *reinterpret_cast<u32x2*>(&X[row][pc + 8]) = u32x2{v[2], v[3]};
     }
     if (wave < 2) {
       const float* p = wave == 0 ? a.g : a.beta;
@@ -432,10 +445,17 @@ __global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigne
 
 // ---------------------------------------------------------------------------
 // Recurrence: carries the state of 32 value channels of one (sequence,
-// value head) through its chunks; wave w of the two owns 16 of them.
+// value head) through its chunks, with three kinds of wave per workgroup:
+//   state waves 0, 1  own 16 channels each and run only the serial chain:
+//                     X = K S0^T, R, Delta = T R, the state update;
+//   output waves 2, 3 get S0 and Delta (bf16 hi/lo) from the state wave of
+//                     the same channels through LDS and form and store
+//                     O = yq * (Q S0^T) + P Delta off the chain;
+//   load waves 4, 5   fetch each chunk's inputs into registers two chunks
+//                     ahead and write them to LDS one chunk ahead.
+// So the state waves never issue a global load or store.
 
-constexpr int kRecNT = 128;  // threads per recurrence workgroup (2 waves)
-constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kRecNT = 384;  // threads per recurrence workgroup: 2 state + 2 output + 2 load waves
 
 // One chunk's shared inputs in LDS (62 KiB; two buffers).  Every region is a
 // whole number of 1 KiB blocks, so one 64-lane direct-to-LDS load (16 bytes
@@ -457,8 +477,15 @@ struct __align__(16) RecBuf {
   uint16_t V[kC][kDVS];
 };
 static_assert(sizeof(RecBuf) == 62 * 1024, "RecBuf must be 62 KiB");
+// State-to-output exchange, one per state wave: S0 hi/lo (8 fragments) and
+// Delta hi/lo (4 fragments), 16 bytes per lane each, stored lane-major.
+struct __align__(16) Xchg {
+  u32x4 S[8][64];
+  u32x4 D[4][64];
+};
+static_assert(sizeof(Xchg) == 12 * 1024, "Xchg must be 12 KiB");
 constexpr int kRecLoads = 62;      // 1 KiB blocks per buffer
-constexpr int kLoadsPerWave = 31;  // block i = wave + 2 jj
+constexpr int kLoadsPerWave = 31;  // block i = lw + 2 jj, lw = load wave 0 or 1
 constexpr int kBlkQ = 16, kBlkM = 32, kBlkF = 56, kBlkV = 58;  // region starts
 static_assert(kBlkQ % 2 == 0 && kBlkM % 2 == 0 && kBlkF % 2 == 0 && kBlkV % 2 == 0,
               "a pair of blocks never straddles two regions");
@@ -470,62 +497,63 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
-// Per-lane parts of the direct-load source offsets (bytes).
+// Per-lane parts of the direct-load source offsets (bytes) of load wave lw.
 struct RecLane {
-  uint32_t kq_e, kq_o;  // k/q block b: row 4b + lane/16, slot (lane%16) ^ kqswz(row); b%4 = wave, wave + 2
+  uint32_t kq_e, kq_o;  // k/q block b: row 4b + lane/16, slot (lane%16) ^ kqswz(row); b%4 = lw, lw + 2
   uint32_t slot0;       // (lane%16) ^ 4 (lane/16)
   uint32_t lane16;      // 16 lane
-  uint32_t fac;         // factor blocks: 16 lane (wave 0), 16 min(lane, 7) (wave 1: e^{G_L} only)
+  uint32_t fac;         // factor blocks: 16 lane (lw 0), 16 min(lane, 7) (lw 1: e^{G_L} only)
   uint32_t v;           // v block b: row 16b + lane/4, slot lane%4
 };
 
-// Issue this wave's direct loads jj0..jj1-1 of one chunk into buf.  kb, qb,
-// vb point at row 0 of the chunk (k, q of the key head; this workgroup's v
-// channels), rb at the chunk record.  kFull: a whole chunk; otherwise rows at
-// or past L repeat row L-1 (they are never used, but must be finite).
+// Source of load wave lw's block jj of one chunk (block i = lw + 2 jj, lane
+// `lane`).  kb, qb, vb point at row 0 of the chunk (k, q of the key head;
+// this workgroup's v channels), rb at the chunk record.  kFull: a whole
+// chunk; otherwise rows at or past L repeat row L-1 (they are never used,
+// but must be finite).
 template <bool kFull>
-__device__ __forceinline__ void rec_issue(RecBuf* buf, const unsigned char* kb, const unsigned char* qb,
-                                          const unsigned char* rb, const unsigned char* vb, const RecLane& ln,
-                                          int wave, int lane, int row_bytes, int vrow_bytes, int L, int jj0,
-                                          int jj1) {
-#pragma unroll
-  for (int jj = 0; jj < kLoadsPerWave; ++jj) {
-    if (jj < jj0 || jj >= jj1) continue;
-    const int i = wave + 2 * jj;
-    const unsigned char* src;
-    uint32_t off;
-    if (2 * jj < kBlkM) {  // k or q: block b covers rows 4b .. 4b+3
-      const int b = 2 * jj < kBlkQ ? i : i - kBlkQ;
-      const unsigned char* base = 2 * jj < kBlkQ ? kb : qb;
-      if (kFull) {
-        src = base + (size_t)(4 * b) * row_bytes;
-        off = (jj & 1) ? ln.kq_o : ln.kq_e;
-      } else {
-        const int row = min(4 * b + (lane >> 4), L - 1);
-        src = base;
-        off = (uint32_t)row * row_bytes + 16 * (ln.slot0 ^ (uint32_t)(b & 3));
-      }
-    } else if (2 * jj < kBlkF) {
-      src = rb + 1024 * (i - kBlkM);
-      off = ln.lane16;
-    } else if (2 * jj < kBlkV) {
-      src = rb + kFacOff + 1024 * wave;
-      off = ln.fac;
-    } else {
-      const int b = i - kBlkV;
-      if (kFull) {
-        src = vb + (size_t)(16 * b) * vrow_bytes;
-        off = ln.v;
-      } else {
-        const int row = min(16 * b + (lane >> 2), L - 1);
-        src = vb;
-        off = (uint32_t)row * vrow_bytes + 16 * (lane & 3);
-      }
-    }
-    lds_void_ptr dst = (lds_void_ptr)(reinterpret_cast<unsigned char*>(buf) + 1024 * i);
-    __builtin_amdgcn_global_load_lds(src + off, dst, 16, 0, 0);
+__device__ __forceinline__ const unsigned char* rec_src(int jj, const unsigned char* kb, const unsigned char* qb,
+                                                        const unsigned char* rb, const unsigned char* vb,
+                                                        const RecLane& ln, int lw, int lane, int row_bytes,
+                                                        int vrow_bytes, int L) {
+  const int i = lw + 2 * jj;
+  if (2 * jj < kBlkM) {  // k or q: block b covers rows 4b .. 4b+3
+    const int b = 2 * jj < kBlkQ ? i : i - kBlkQ;
+    const unsigned char* base = 2 * jj < kBlkQ ? kb : qb;
+    if (kFull) return base + (size_t)(4 * b) * row_bytes + ((jj & 1) ? ln.kq_o : ln.kq_e);
+    const int row = min(4 * b + (lane >> 4), L - 1);
+    return base + (size_t)row * row_bytes + 16 * (ln.slot0 ^ (uint32_t)(b & 3));
   }
+  if (2 * jj < kBlkF) return rb + 1024 * (i - kBlkM) + ln.lane16;
+  if (2 * jj < kBlkV) return rb + kFacOff + 1024 * lw + ln.fac;
+  const int b = i - kBlkV;
+  if (kFull) return vb + (size_t)(16 * b) * vrow_bytes + ln.v;
+  const int row = min(16 * b + (lane >> 2), L - 1);
+  return vb + (size_t)row * vrow_bytes + 16 * (lane & 3);
 }
+
+// Load wave lw's blocks jj0..jj1-1 of one chunk into registers, and from there into
+// an LDS buffer (each lane's 16 bytes of block i land at 1024 i + 16 lane).
+template <bool kFull>
+__device__ __forceinline__ void rec_fetch(u32x4* stage, const unsigned char* kb, const unsigned char* qb,
+                                          const unsigned char* rb, const unsigned char* vb, const RecLane& ln,
+                                          int lw, int lane, int row_bytes, int vrow_bytes, int L, int jj0, int jj1) {
+#pragma unroll
+  for (int jj = 0; jj < kLoadsPerWave; ++jj)
+    if (jj >= jj0 && jj < jj1)
+      stage[jj] = *reinterpret_cast<const u32x4*>(
+        rec_src<kFull>(jj, kb, qb, rb, vb, ln, lw, lane, row_bytes, vrow_bytes, L));
+}
+__device__ __forceinline__ void rec_put(RecBuf* buf, const u32x4* stage, int lw, int lane) {
+#pragma unroll
+  for (int jj = 0; jj < kLoadsPerWave; ++jj)
+    *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(buf) + 1024 * (lw + 2 * jj) + 16 * lane) = stage[jj];
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses,
+// not for its global loads and stores (which __syncthreads() would also wait
+// for), so loads can stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Output stores of tiles ti0..ti1-1 of one chunk: Ot[ti][i] is the output of
 // token 16 ti + c at value channel 4 q4 + i of this wave's 16, so each lane
@@ -592,8 +620,11 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
   extern __shared__ __align__(16) unsigned char smem_raw[];
   RecBuf* bufs = reinterpret_cast<RecBuf*>(smem_raw);
 
+  Xchg* xch = reinterpret_cast<Xchg*>(smem_raw + 2 * sizeof(RecBuf));
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int role = wv >> 1;  // 0 state, 1 output, 2 load
+  const int wave = wv & 1;   // channel group of a state/output wave, or load wave index lw
   const int c = lane & 15, q4 = lane >> 4;
   // Workgroup -> (sequence, value head, slice), XCD-aware: consecutive
   // workgroup ids go round-robin to the 8 XCDs, each with its own L2, so the
@@ -662,111 +693,170 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
                 ? *reinterpret_cast<const f32x4*>(a.initial_state + sbase + 32 * (kt >> 1) + 4 * (kt & 1))
                 : f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Direct loads of loads jj0..jj1-1 of the chunk at token cc (index jc) into nb.
-  auto issue = [&](RecBuf* nb, int cc, int jc, int jj0, int jj1) {
-    const int Lc = min(kC, eos - cc);
-    const unsigned char* nk = reinterpret_cast<const unsigned char*>(kg + (size_t)cc * kqts);
-    const unsigned char* nq = reinterpret_cast<const unsigned char*>(qg + (size_t)cc * kqts);
-    const unsigned char* nv = reinterpret_cast<const unsigned char*>(vg + (size_t)cc * vts);
-    const unsigned char* nr = recs + (size_t)jc * rstride;
-    if (Lc == kC) rec_issue<true>(nb, nk, nq, nr, nv, ln, wave, lane, row_bytes, vrow_bytes, kC, jj0, jj1);
-    else rec_issue<false>(nb, nk, nq, nr, nv, ln, wave, lane, row_bytes, vrow_bytes, Lc, jj0, jj1);
-  };
-  if (bos < eos) issue(bufs, bos, jb, 0, kLoadsPerWave);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  if (role == 2) {
+    // Load waves.  Chunk j+1 is written into the buffer of chunk j-1 after the
+    // first barrier of iteration j (the other waves are then done with that
+    // buffer) and is complete at the second.  Its global loads are issued
+    // during iteration j-1, half before and half after its second barrier, so
+    // their latency is hidden and issuing them delays neither barrier.
+    u32x4 stage[kLoadsPerWave];
+    auto fetch = [&](int cc, int jc, int jj0, int jj1) {
+      const int Lc = min(kC, eos - cc);
+      const unsigned char* nk = reinterpret_cast<const unsigned char*>(kg + (size_t)cc * kqts);
+      const unsigned char* nq = reinterpret_cast<const unsigned char*>(qg + (size_t)cc * kqts);
+      const unsigned char* nv = reinterpret_cast<const unsigned char*>(vg + (size_t)cc * vts);
+      const unsigned char* nr = recs + (size_t)jc * rstride;
+      if (Lc == kC) rec_fetch<true>(stage, nk, nq, nr, nv, ln, wave, lane, row_bytes, vrow_bytes, kC, jj0, jj1);
+      else rec_fetch<false>(stage, nk, nq, nr, nv, ln, wave, lane, row_bytes, vrow_bytes, Lc, jj0, jj1);
+    };
+    if (bos < eos) {
+      fetch(bos, jb, 0, kLoadsPerWave);
+      rec_put(bufs, stage, wave, lane);
+      if (bos + kC < eos) fetch(bos + kC, jb + 1, 0, kLoadsPerWave);
+    }
+    lds_barrier();
+    int it = 0;
+    for (int c0 = bos, j = jb; c0 < eos; c0 += kC, ++j, ++it) {
+      lds_barrier();
+      if (c0 + kC < eos) rec_put(bufs + ((it & 1) ^ 1), stage, wave, lane);
+      constexpr int kHalf = kLoadsPerWave / 2;
+      if (c0 + 2 * kC < eos) fetch(c0 + 2 * kC, j + 2, 0, kHalf);
+      lds_barrier();
+      if (c0 + 2 * kC < eos) fetch(c0 + 2 * kC, j + 2, kHalf, kLoadsPerWave);
+    }
+    return;
+  }
+  lds_barrier();
 
-  // The transposing LDS reads come first in each iteration, while no direct
-  // load or store is in flight: the compiler waits for every outstanding
-  // vector memory operation before them.  So the state update of chunk j-1
-  // (which reads chunk j-1's k tile) opens iteration j, and the prefetch of
-  // chunk j+1 into that buffer follows a barrier.
-  f32x4 Oprev[4];
+  // Delta = T R and P Delta need the six nonzero 32-wide steps of the block
+  // lower triangle, (ti, ks) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
+  auto mrd = [&](const unsigned char* bb, int m, int ti, int ks) {
+    const int o = ti < 2 ? mA + 1024 * ti : (ks ? mB1 : mB0) + 2048 * (ti - 2);
+    return lds8(reinterpret_cast<const uint16_t*>(bb + offsetof(RecBuf, M) + m * kMatBytes + o));
+  };
+  Xchg& X = xch[wave];
+
+  if (role == 1) {
+    // Output waves: O^T = yq * (S0 Q^T) + Delta^T P^T for the channels of
+    // state wave `wave`, transposed so each lane stores 4 adjacent channels.
+    int it = 0;
+    for (int c0 = bos; c0 < eos; c0 += kC, ++it) {
+      const int L = min(kC, eos - c0);
+      const unsigned char* bb = reinterpret_cast<const unsigned char*>(&bufs[it & 1]);
+      const RecBuf& B = bufs[it & 1];
+      lds_barrier();  // S0 of this chunk is in the exchange
+      bf16x8 sbh[4], sbl[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        sbh[ks] = __builtin_bit_cast(bf16x8, X.S[ks][lane]);
+        sbl[ks] = __builtin_bit_cast(bf16x8, X.S[4 + ks][lane]);
+      }
+      f32x4 Y[4];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 aq = lds8(reinterpret_cast<const uint16_t*>(bb + offsetof(RecBuf, Q) + xo[ks] + 4096 * ti));
+          y = mfma16x16x32(sbh[ks], aq, y);
+          y = mfma16x16x32(sbl[ks], aq, y);
+        }
+        Y[ti] = y * B.fac[2][16 * ti + c];  // Y^T: token 16 ti + c
+      }
+      bf16x8 ph[6], pl[6];
+#pragma unroll
+      for (int u = 0; u < 6; ++u) {
+        const int ti = u < 2 ? u : 2 + (u - 2) / 2, ks = u < 2 ? 0 : (u - 2) % 2;
+        ph[u] = mrd(bb, 2, ti, ks);
+        pl[u] = mrd(bb, 3, ti, ks);
+      }
+      lds_barrier();  // Delta of this chunk is in the exchange
+      bf16x8 dbh[2], dbl[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dbh[ks] = __builtin_bit_cast(bf16x8, X.D[ks][lane]);
+        dbl[ks] = __builtin_bit_cast(bf16x8, X.D[2 + ks][lane]);
+      }
+      f32x4 O[4];
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        f32x4 y = Y[ti];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (2 * ks > ti) continue;
+          const int u = ti < 2 ? ti : 2 + 2 * (ti - 2) + ks;
+          y = mfma3(dbh[ks], dbl[ks], ph[u], pl[u], y);
+        }
+        O[ti] = y;
+      }
+      store_out(og + (size_t)(c0 - bos) * vts, vts, O, L, c, 0, 4);
+    }
+    return;
+  }
+
+  // State waves.  The transposing LDS reads (state update, v) are safe from
+  // the compiler's wait for outstanding vector memory operations: these waves
+  // issue none.  The state update of chunk j-1 (which reads chunk j-1's k
+  // tile) opens iteration j.
   bf16x8 dph[2], dpl[2];  // Delta' of the previous chunk, for its state update
-  int pL = 0;
   int it = 0;
-  for (int c0 = bos, j = jb; c0 < eos; c0 += kC, ++j, ++it) {
-    const int L = min(kC, eos - c0);
+  for (int c0 = bos; c0 < eos; c0 += kC, ++it) {
     RecBuf& B = bufs[it & 1];
     RecBuf* NB = bufs + ((it & 1) ^ 1);  // chunk j-1's inputs, then chunk j+1's
     const unsigned char* bb = reinterpret_cast<const unsigned char*>(&B);
-    const bool more = c0 + kC < eos;
     if (it > 0) state_update(s, *NB, dph, dpl, tro);
+    bf16x8 sbh[4], sbl[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      split8(s[2 * ks], s[2 * ks + 1], sbh[ks], sbl[ks]);
+      X.S[ks][lane] = __builtin_bit_cast(u32x4, sbh[ks]);
+      X.S[4 + ks][lane] = __builtin_bit_cast(u32x4, sbl[ks]);
+    }
     // v[16 ti + 4 q4 + e][vcol], e = 0..3, one transposing read per tile
     v4i16 vt[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
       vt[ti] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_v4i16_ptr)(reinterpret_cast<const unsigned char*>(&B.V[0][0]) + vto + 1024 * ti));
-    __syncthreads();  // every wave is done with chunk j-1's buffer
-    TO* oprev = og + (size_t)(c0 - kC - bos) * vts;
+    lds_barrier();  // done with chunk j-1's buffer; S0 is in the exchange
 
-    // ---- state phase: this wave's 16 value channels
-    bf16x8 sbh[4], sbl[4];
+    // X = K S0^T (tokens x channels); the k fragments of tile ti + 1 are read
+    // while tile ti multiplies
+    auto rd_k = [&](int ti, bf16x8* fk) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) split8(s[2 * ks], s[2 * ks + 1], sbh[ks], sbl[ks]);
-
-    // X = K S0^T (tokens x channels) and Y^T = S0 Q^T (channels x tokens);
-    // the k and q fragments of tile ti + 1 are read while tile ti multiplies
-    auto rd_kq = [&](int ti, bf16x8* fk, bf16x8* fq) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 4; ++ks)
         fk[ks] = lds8(reinterpret_cast<const uint16_t*>(bb + offsetof(RecBuf, K) + xo[ks] + 4096 * ti));
-        fq[ks] = lds8(reinterpret_cast<const uint16_t*>(bb + offsetof(RecBuf, Q) + xo[ks] + 4096 * ti));
-      }
     };
-    bf16x8 fk[2][4], fq[2][4];
-    rd_kq(0, fk[0], fq[0]);
-    f32x4 R[4], Y[4];
+    bf16x8 fk[2][4];
+    rd_k(0, fk[0]);
+    bf16x8 th[6], tl[6];
+#pragma unroll
+    for (int u = 0; u < 6; ++u) {
+      const int ti = u < 2 ? u : 2 + (u - 2) / 2, ks = u < 2 ? 0 : (u - 2) % 2;
+      th[u] = mrd(bb, 0, ti, ks);
+      tl[u] = mrd(bb, 1, ti, ks);
+    }
+    f32x4 R[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
-      if (ti < 3) rd_kq(ti + 1, fk[(ti + 1) & 1], fq[(ti + 1) & 1]);
+      if (ti < 3) rd_k(ti + 1, fk[(ti + 1) & 1]);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 ak = fk[ti & 1][ks], aq = fq[ti & 1][ks];
-        acc = mfma16x16x32(ak, sbh[ks], acc);
-        y = mfma16x16x32(sbh[ks], aq, y);
-        acc = mfma16x16x32(ak, sbl[ks], acc);
-        y = mfma16x16x32(sbl[ks], aq, y);
+        acc = mfma16x16x32(fk[ti & 1][ks], sbh[ks], acc);
+        acc = mfma16x16x32(fk[ti & 1][ks], sbl[ks], acc);
       }
-      // prefetch of the next chunk and stores of the previous chunk's
-      // outputs, spread over the state phase
-      if (more) issue(NB, c0 + kC, j + 1, 8 * ti, min(8 * ti + 8, kLoadsPerWave));
-      if (it > 0 && (ti & 1)) store_out(oprev, vts, Oprev, pL, c, ti - 1, ti + 1);
       const f32x4 btv = *reinterpret_cast<const f32x4*>(&B.fac[0][16 * ti + 4 * q4]);
       const f32x4 xrv = *reinterpret_cast<const f32x4*>(&B.fac[1][16 * ti + 4 * q4]);
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4)
         R[ti][i4] = btv[i4] * __uint_as_float((uint32_t)(uint16_t)vt[ti][i4] << 16) - xrv[i4] * acc[i4];
-      Y[ti] = y * B.fac[2][16 * ti + c];  // Y^T: token 16 ti + c
     }
-
     bf16x8 rbh[2], rbl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) split8(R[2 * ks], R[2 * ks + 1], rbh[ks], rbl[ks]);
 
-    // Delta = T R; T is block lower triangular, so 32-wide steps above the
-    // diagonal are skipped
-    auto mrd = [&](int m, int ti, int ks) {
-      const int o = ti < 2 ? mA + 1024 * ti : (ks ? mB1 : mB0) + 2048 * (ti - 2);
-      return lds8(reinterpret_cast<const uint16_t*>(bb + offsetof(RecBuf, M) + m * kMatBytes + o));
-    };
-    // the six nonzero 32-wide steps (ti, ks) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-    bf16x8 th[6], tl[6], ph[6], pl[6];
-#pragma unroll
-    for (int u = 0; u < 6; ++u) {
-      const int ti = u < 2 ? u : 2 + (u - 2) / 2, ks = u < 2 ? 0 : (u - 2) % 2;
-      th[u] = mrd(0, ti, ks);
-      tl[u] = mrd(1, ti, ks);
-    }
-#pragma unroll
-    for (int u = 0; u < 6; ++u) {
-      const int ti = u < 2 ? u : 2 + (u - 2) / 2, ks = u < 2 ? 0 : (u - 2) % 2;
-      ph[u] = mrd(2, ti, ks);
-      pl[u] = mrd(3, ti, ks);
-    }
+    // Delta = T R (block lower triangular: steps above the diagonal skipped)
     f32x4 Dl[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
@@ -779,36 +869,19 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
       }
       Dl[ti] = acc;
     }
-    bf16x8 dbh[2], dbl[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      split8(Dl[2 * ks], Dl[2 * ks + 1], dbh[ks], dbl[ks]);
+      bf16x8 dbh, dbl;
+      split8(Dl[2 * ks], Dl[2 * ks + 1], dbh, dbl);
+      X.D[ks][lane] = __builtin_bit_cast(u32x4, dbh);
+      X.D[2 + ks][lane] = __builtin_bit_cast(u32x4, dbl);
       const f32x4 cl0 = *reinterpret_cast<const f32x4*>(&B.fac[3][32 * ks + 4 * q4]);
       const f32x4 cl1 = *reinterpret_cast<const f32x4*>(&B.fac[3][32 * ks + 16 + 4 * q4]);
       split8(Dl[2 * ks] * cl0, Dl[2 * ks + 1] * cl1, dph[ks], dpl[ks]);
     }
-
-    // outputs, transposed: O^T = yq * (S0 Q^T) + Delta^T P^T (stored during
-    // the next chunk)
-#pragma unroll
-    for (int ti = 0; ti < 4; ++ti) {
-      f32x4 y = Y[ti];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (2 * ks > ti) continue;
-        const int u = ti < 2 ? ti : 2 + 2 * (ti - 2) + ks;
-        y = mfma3(dbh[ks], dbl[ks], ph[u], pl[u], y);
-      }
-      Oprev[ti] = y;
-    }
-    pL = L;
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    lds_barrier();  // Delta is in the exchange; the next chunk's inputs are in LDS
   }
-  if (it > 0) {
-    state_update(s, bufs[(it - 1) & 1], dph, dpl, tro);
-    store_out(og + (size_t)(eos - pL - bos) * vts, vts, Oprev, pL, c, 0, 4);
-  }
+  if (it > 0) state_update(s, bufs[(it - 1) & 1], dph, dpl, tro);
 
   if (a.final_state) {
 #pragma unroll
@@ -820,7 +893,7 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
 template <typename TO>
 hipError_t launch_rec_t(const ChunkArgs& a, const unsigned char* ws, hipStream_t st) {
   auto kern = chunk_rec_kernel<TO>;
-  const size_t smem = 2 * sizeof(RecBuf);  // 124 KiB: double-buffered chunk inputs
+  const size_t smem = 2 * sizeof(RecBuf) + 2 * sizeof(Xchg);  // 148 KiB: double-buffered inputs + exchange
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
@@ -854,7 +927,7 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, void* workspace, hipStream_t st
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_prep_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)nch, a.Hv), dim3(kNT), smem, st, a, ws);
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)(nch * a.Hv)), dim3(kNT), smem, st, a, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
