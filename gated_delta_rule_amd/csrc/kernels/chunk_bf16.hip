@@ -90,6 +90,9 @@ __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_
   h[0] = (__bf16)x0;
   h[1] = (__bf16)x1;
   hi = __builtin_bit_cast(uint32_t, h);
+  // keep the packed conversion: the halves below come from it (one
+  // instruction each) instead of a second conversion of x0
+  asm("" : "+v"(hi));
   const float r0 = x0 - __uint_as_float(hi << 16);
   const float r1 = x1 - __uint_as_float(hi & 0xffff0000u);
   bf16x2 l;
@@ -696,9 +699,8 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
   if (role == 2) {
     // Load waves.  Chunk j+1 is written into the buffer of chunk j-1 after the
     // first barrier of iteration j (the other waves are then done with that
-    // buffer) and is complete at the second.  Its global loads are issued
-    // during iteration j-1, half before and half after its second barrier, so
-    // their latency is hidden and issuing them delays neither barrier.
+    // buffer) and is complete at the second.  Its global loads were issued
+    // during iteration j-1, so their latency is hidden.
     u32x4 stage[kLoadsPerWave];
     auto fetch = [&](int cc, int jc, int jj0, int jj1) {
       const int Lc = min(kC, eos - cc);
@@ -719,12 +721,20 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
     for (int c0 = bos, j = jb; c0 < eos; c0 += kC, ++j, ++it) {
       lds_barrier();
       if (c0 + kC < eos) rec_put(bufs + ((it & 1) ^ 1), stage, wave, lane);
-      constexpr int kHalf = kLoadsPerWave / 2;
-      if (c0 + 2 * kC < eos) fetch(c0 + 2 * kC, j + 2, 0, kHalf);
+      // the record, factor and v blocks (from HBM) right away, the k and q
+      // blocks (shared with neighbouring workgroups through L2) after the
+      // second barrier
+      constexpr int kKQ = kBlkM / 2;
+      if (c0 + 2 * kC < eos) fetch(c0 + 2 * kC, j + 2, kKQ, kLoadsPerWave);
       lds_barrier();
-      if (c0 + 2 * kC < eos) fetch(c0 + 2 * kC, j + 2, kHalf, kLoadsPerWave);
+      if (c0 + 2 * kC < eos) fetch(c0 + 2 * kC, j + 2, 0, kKQ);
     }
     return;
+  }
+  if (role == 0) {
+    u32x4* k1 = reinterpret_cast<u32x4*>(&bufs[1].K[0][0]);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) k1[(8 * wave + r) * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
   }
   lds_barrier();
 
@@ -751,6 +761,9 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
         sbh[ks] = __builtin_bit_cast(bf16x8, X.S[ks][lane]);
         sbl[ks] = __builtin_bit_cast(bf16x8, X.S[4 + ks][lane]);
       }
+      lds_barrier();  // Delta of this chunk is in the exchange
+      // Y^T (token 16 ti + c) and the outputs, after the second barrier: the
+      // chunk's q, P and factors stay in LDS until the next first barrier
       f32x4 Y[4];
 #pragma unroll
       for (int ti = 0; ti < 4; ++ti) {
@@ -761,7 +774,7 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
           y = mfma16x16x32(sbh[ks], aq, y);
           y = mfma16x16x32(sbl[ks], aq, y);
         }
-        Y[ti] = y * B.fac[2][16 * ti + c];  // Y^T: token 16 ti + c
+        Y[ti] = y * B.fac[2][16 * ti + c];
       }
       bf16x8 ph[6], pl[6];
 #pragma unroll
@@ -770,7 +783,6 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
         ph[u] = mrd(bb, 2, ti, ks);
         pl[u] = mrd(bb, 3, ti, ks);
       }
-      lds_barrier();  // Delta of this chunk is in the exchange
       bf16x8 dbh[2], dbl[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -796,39 +808,80 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
 
   // State waves.  The transposing LDS reads (state update, v) are safe from
   // the compiler's wait for outstanding vector memory operations: these waves
-  // issue none.  The state update of chunk j-1 (which reads chunk j-1's k
-  // tile) opens iteration j.
+  // issue none.  Iteration j runs the state update of chunk j-1 (k^T from
+  // chunk j-1's buffer) fused with chunk j's X = K S0^T, one 32-wide key step
+  // at a time: update state tiles 2 ks and 2 ks + 1, split them to bf16
+  // hi/lo (also for the output waves), multiply them into X.  So the matrix
+  // core has independent work while each step's split runs.
+  // Before the first chunk there is no previous one: its state update must
+  // leave S as it is, so Delta' starts at zero and the k tile of the unused
+  // second buffer is zero-filled (the load waves first write that buffer
+  // after the first barrier).
   bf16x8 dph[2], dpl[2];  // Delta' of the previous chunk, for its state update
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    dph[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    dpl[ks] = dph[ks];
+  }
   int it = 0;
   for (int c0 = bos; c0 < eos; c0 += kC, ++it) {
     RecBuf& B = bufs[it & 1];
     RecBuf* NB = bufs + ((it & 1) ^ 1);  // chunk j-1's inputs, then chunk j+1's
     const unsigned char* bb = reinterpret_cast<const unsigned char*>(&B);
-    if (it > 0) state_update(s, *NB, dph, dpl, tro);
-    bf16x8 sbh[4], sbl[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      split8(s[2 * ks], s[2 * ks + 1], sbh[ks], sbl[ks]);
-      X.S[ks][lane] = __builtin_bit_cast(u32x4, sbh[ks]);
-      X.S[4 + ks][lane] = __builtin_bit_cast(u32x4, sbl[ks]);
-    }
+    const unsigned char* nkb = reinterpret_cast<const unsigned char*>(&NB->K[0][0]);
     // v[16 ti + 4 q4 + e][vcol], e = 0..3, one transposing read per tile
     v4i16 vt[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti)
       vt[ti] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_v4i16_ptr)(reinterpret_cast<const unsigned char*>(&B.V[0][0]) + vto + 1024 * ti));
+    // fragments of key step ks: k rows of the 4 token tiles (X), and k^T of
+    // state tiles 2 ks, 2 ks + 1 for both 32-token halves (state update)
+    auto rd_k = [&](int ks, bf16x8* fk) {
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti)
+        fk[ti] = lds8(reinterpret_cast<const uint16_t*>(bb + offsetof(RecBuf, K) + xo[ks] + 4096 * ti));
+    };
+    auto rd_kt = [&](int ks, bf16x8* ft) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // u = 2 hh + ks2
+        const int o = tro[ks] + 8 * (u >> 1) + 256 * 32 * (u & 1);
+        ft[u] = tr_frag(nkb, o, o + 256 * 16);
+      }
+    };
+    const float eGL = it > 0 ? NB->eGL[0] : 1.f;
+    bf16x8 fk[2][4], ft[2][4];
+    rd_k(0, fk[0]);
+    rd_kt(0, ft[0]);
+    f32x4 Xa[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) {
+        rd_k(ks + 1, fk[(ks + 1) & 1]);
+        rd_kt(ks + 1, ft[(ks + 1) & 1]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        f32x4 acc = s[2 * ks + hh] * eGL;
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+          acc = mfma16x16x32(ft[ks & 1][2 * hh + ks2], dph[ks2], acc);
+          acc = mfma16x16x32(ft[ks & 1][2 * hh + ks2], dpl[ks2], acc);
+        }
+        s[2 * ks + hh] = acc;
+      }
+      bf16x8 sbh, sbl;
+      split8(s[2 * ks], s[2 * ks + 1], sbh, sbl);
+      X.S[ks][lane] = __builtin_bit_cast(u32x4, sbh);
+      X.S[4 + ks][lane] = __builtin_bit_cast(u32x4, sbl);
+#pragma unroll
+      for (int ti = 0; ti < 4; ++ti) {
+        Xa[ti] = mfma16x16x32(fk[ks & 1][ti], sbh, Xa[ti]);
+        Xa[ti] = mfma16x16x32(fk[ks & 1][ti], sbl, Xa[ti]);
+      }
+    }
     lds_barrier();  // done with chunk j-1's buffer; S0 is in the exchange
 
-    // X = K S0^T (tokens x channels); the k fragments of tile ti + 1 are read
-    // while tile ti multiplies
-    auto rd_k = [&](int ti, bf16x8* fk) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        fk[ks] = lds8(reinterpret_cast<const uint16_t*>(bb + offsetof(RecBuf, K) + xo[ks] + 4096 * ti));
-    };
-    bf16x8 fk[2][4];
-    rd_k(0, fk[0]);
     bf16x8 th[6], tl[6];
 #pragma unroll
     for (int u = 0; u < 6; ++u) {
@@ -839,18 +892,11 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
     f32x4 R[4];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
-      if (ti < 3) rd_k(ti + 1, fk[(ti + 1) & 1]);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        acc = mfma16x16x32(fk[ti & 1][ks], sbh[ks], acc);
-        acc = mfma16x16x32(fk[ti & 1][ks], sbl[ks], acc);
-      }
       const f32x4 btv = *reinterpret_cast<const f32x4*>(&B.fac[0][16 * ti + 4 * q4]);
       const f32x4 xrv = *reinterpret_cast<const f32x4*>(&B.fac[1][16 * ti + 4 * q4]);
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4)
-        R[ti][i4] = btv[i4] * __uint_as_float((uint32_t)(uint16_t)vt[ti][i4] << 16) - xrv[i4] * acc[i4];
+        R[ti][i4] = btv[i4] * __uint_as_float((uint32_t)(uint16_t)vt[ti][i4] << 16) - xrv[i4] * Xa[ti][i4];
     }
     bf16x8 rbh[2], rbl[2];
 #pragma unroll
