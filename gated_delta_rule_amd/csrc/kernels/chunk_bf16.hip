@@ -80,6 +80,11 @@ __device__ __forceinline__ int compact_idx(int i, int p) {
                 : 1024 + (i - 32) * 64 + 8 * ((p >> 3) ^ (i & 7)) + (p & 7);
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses,
+// not for its global loads and stores (which __syncthreads() would also wait
+// for), so loads and stores can stay in flight across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ bf16x8 lds8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
 }
@@ -205,18 +210,26 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
 // Chunk preparation: T = (I + A)^{-1}, P and token factors of one
 // (chunk, value head).
 
+// LDS of chunk_prep_kernel (36 KiB, so four workgroups share a compute
+// unit): k and q rows are dead once the Gram tiles are in registers, so A and
+// T reuse their space; the 16x16 and 32x32 products of the merges are staged
+// in A's never-used upper right 32x32 block (rows 0..31, columns 32..63).
 struct __align__(16) PrepSmem {
-  uint16_t Kr[kC][kD + 8];   // k rows, columns permuted
-  uint16_t Qr[kC][kD + 8];   // q rows, columns permuted
-  float A[kC][kC + 4];
-  float Tf[kC][kC + 4];
-  float Ys[32][36];
+  union {
+    uint16_t Kr[kC][kD + 8];  // k rows, columns permuted
+    float A[kC][kC + 4];
+  };
+  union {
+    uint16_t Qr[kC][kD + 8];  // q rows, columns permuted
+    float Tf[kC][kC + 4];
+  };
   float ssk[kC], ssq[kC];
   float G2[kC], rk[kC], ar[kC], pr[kC];
-  float gin[kC], bin[kC];
+  float bin[kC];
 };
+static_assert(sizeof(PrepSmem) <= 40 * 1024, "four prepare workgroups per compute unit");
 
-__global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigned char* ws) {
+__global__ __launch_bounds__(kNT, 4) void chunk_prep_kernel(ChunkArgs a, unsigned char* ws) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -247,13 +260,28 @@ __global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigne
     uint16_t(*X)[kD + 8] = tid < 128 ? sm.Kr : sm.Qr;
     const int b = tid & 127, rb = b >> 4, cb = b & 15;
     const int pc = perm8(cb);
-    // all eight loads in flight before the LDS stores; rows past L read row
-    // L-1 (in bounds) and are zeroed
+    // g (wave 0) or beta (wave 1) of token `lane` first, then all eight k/q
+    // loads in flight before the LDS stores; rows past L read row L-1 (in
+    // bounds) and are zeroed
+    float gv = 0.f;
+    if (wave < 2 && lane < L) gv = (wave == 0 ? a.g : a.beta)[(size_t)(c0 + lane) * a.Hv + h];
     u32x4 w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = min(8 * rb + i, L - 1);
       w[i] = *reinterpret_cast<const u32x4*>(src + ((size_t)(c0 + row) * a.Hk + kh) * kD + 8 * cb);
+    }
+    if (wave == 1) sm.bin[lane] = gv;
+    if (wave == 0) {
+      // chunk-local cumulative log-decay, summed in fp64 while the k/q loads
+      // are in flight; kept as log2 (G * log2 e)
+      double G = (double)gv;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(G, off, 64);
+        if (lane >= off) G += o;
+      }
+      sm.G2[lane] = (float)(G * 1.4426950408889634);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -262,12 +290,8 @@ __global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigne
       *reinterpret_cast<u32x2*>(&X[row][pc]) = u32x2{v[0], v[1]};
       *reinterpret_cast<u32x2*>(&X[row][pc + 8]) = u32x2{v[2], v[3]};
     }
-    if (wave < 2) {
-      const float* p = wave == 0 ? a.g : a.beta;
-      (wave == 0 ? sm.gin : sm.bin)[lane] = lane < L ? p[(size_t)(c0 + lane) * a.Hv + h] : 0.f;
-    }
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- Gram tiles (raw bf16 products): job 0..9 K_j K_i^T, 10..19 K_j Q_i^T,
   // 20..23 Q_i Q_i^T (diagonal only, for the q norms).  Lane holds
@@ -302,23 +326,16 @@ __global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigne
     }
     if (ti == tj && (job < 10 || job >= 20) && (c >> 2) == q4) (job < 10 ? sm.ssk : sm.ssq)[16 * ti + c] = acc[c & 3];
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- per-token factors (wave 0): norms, fp64 cumulative decay, scales
+  // ---- per-token factors (wave 0): norms and scales
   if (wave == 0) {
     const float rkv = a.use_l2 ? 1.f / sqrtf(sm.ssk[lane] + a.eps) : 1.f;
     const float rqv = a.use_l2 ? 1.f / sqrtf(sm.ssq[lane] + a.eps) : 1.f;
-    double G = (double)sm.gin[lane];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double o = __shfl_up(G, off, 64);
-      if (lane >= off) G += o;
-    }
-    const float g2 = (float)(G * 1.4426950408889634);
-    const float g2L = __shfl(g2, 63, 64);
+    const float g2 = sm.G2[lane];
+    const float g2L = sm.G2[63];
     const float eG = exp2f(g2);
     const float bv = sm.bin[lane];
-    sm.G2[lane] = g2;
     sm.rk[lane] = rkv;
     sm.ar[lane] = bv * rkv;
     sm.pr[lane] = a.scale * rqv;
@@ -328,7 +345,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigne
     facg[192 + lane] = rkv * exp2f(g2L - g2);  // cL
     if (lane == 0) facg[256] = exp2f(g2L);   // e^{G_L}
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- scale Gram tiles into A (fp32, LDS) and P (hi/lo bf16, workspace)
 #pragma unroll
@@ -346,7 +363,10 @@ __global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigne
     for (int e = 0; e < 4; ++e) {
       const int jj = j0 + e;
       const bool keep = job < 10 ? (jj < i) : (jj <= i);
-      val[e] = keep ? rowf * rkj[e] * exp2f(g2i - g2j[e]) * gacc[u][e] : 0.f;
+      // exponent <= 0 where kept; the hardware exp2 may flush results below
+      // 2^-126 to zero, far under the precision these entries carry
+      const float x = rowf * rkj[e] * __builtin_amdgcn_exp2f(g2i - g2j[e]) * gacc[u][e];
+      val[e] = keep ? x : 0.f;
     }
     if (job < 10) {
       *reinterpret_cast<f32x4*>(&sm.A[i][j0]) = val;
@@ -366,7 +386,7 @@ __global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigne
     *reinterpret_cast<u32x2*>(Plg + off) = u32x2{0u, 0u};
     *reinterpret_cast<f32x4*>(&sm.Tf[i][32 * wave + 16 + 4 * q4]) = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution
   // (wave w inverts block w; lane c < 16 computes column c)
@@ -394,37 +414,37 @@ __global__ __launch_bounds__(kNT, 2) void chunk_prep_kernel(ChunkArgs a, unsigne
 #pragma unroll
     for (int r = 0; r < 16; ++r) sm.Tf[16 * b + r][16 * b + c] = x[r];
   }
-  __syncthreads();
+  lds_barrier();
   // level 1: T_{p+1,p} = -T_{p+1,p+1} (A_{p+1,p} T_{p,p}), p = 0, 32 (waves 0, 1)
   if (wave < 2) {
     const int p = 32 * wave;
     const f32x4 y = tile_mm_f32<16>(&sm.A[p + 16][p], kC + 4, &sm.Tf[p][p], kC + 4, c, q4);
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) sm.Ys[16 * wave + 4 * q4 + i4][c] = y[i4];
+    for (int i4 = 0; i4 < 4; ++i4) sm.A[16 * wave + 4 * q4 + i4][32 + c] = y[i4];
   }
-  __syncthreads();
+  lds_barrier();
   if (wave < 2) {
     const int p = 32 * wave;
-    const f32x4 t = tile_mm_f32<16>(&sm.Tf[p + 16][p + 16], kC + 4, &sm.Ys[16 * wave][0], 36, c, q4);
+    const f32x4 t = tile_mm_f32<16>(&sm.Tf[p + 16][p + 16], kC + 4, &sm.A[16 * wave][32], kC + 4, c, q4);
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) sm.Tf[p + 16 + 4 * q4 + i4][p + c] = -t[i4];
   }
-  __syncthreads();
+  lds_barrier();
   // level 2: T_{2:4,0:2} = -T_{2:4,2:4} (A_{2:4,0:2} T_{0:2,0:2}), one 16x16 tile per wave
   {
     const int yi = wave >> 1, yj = wave & 1;
     const f32x4 y = tile_mm_f32<32>(&sm.A[32 + 16 * yi][0], kC + 4, &sm.Tf[0][16 * yj], kC + 4, c, q4);
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) sm.Ys[16 * yi + 4 * q4 + i4][16 * yj + c] = y[i4];
+    for (int i4 = 0; i4 < 4; ++i4) sm.A[16 * yi + 4 * q4 + i4][32 + 16 * yj + c] = y[i4];
   }
-  __syncthreads();
+  lds_barrier();
   {
     const int xi = wave >> 1, xj = wave & 1;
-    const f32x4 t = tile_mm_f32<32>(&sm.Tf[32 + 16 * xi][32], kC + 4, &sm.Ys[0][16 * xj], 36, c, q4);
+    const f32x4 t = tile_mm_f32<32>(&sm.Tf[32 + 16 * xi][32], kC + 4, &sm.A[0][32 + 16 * xj], kC + 4, c, q4);
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) sm.Tf[32 + 16 * xi + 4 * q4 + i4][16 * xj + c] = -t[i4];
   }
-  __syncthreads();
+  lds_barrier();
   // T to hi/lo bf16 over the lower 32x32-block triangle (the upper parts of
   // the diagonal blocks are zero and are read by 32-wide steps)
 #pragma unroll
@@ -552,11 +572,6 @@ __device__ __forceinline__ void rec_put(RecBuf* buf, const u32x4* stage, int lw,
   for (int jj = 0; jj < kLoadsPerWave; ++jj)
     *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(buf) + 1024 * (lw + 2 * jj) + 16 * lane) = stage[jj];
 }
-
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses,
-// not for its global loads and stores (which __syncthreads() would also wait
-// for), so loads can stay in flight across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Output stores of tiles ti0..ti1-1 of one chunk: Ot[ti][i] is the output of
 // token 16 ti + c at value channel 4 q4 + i of this wave's 16, so each lane
