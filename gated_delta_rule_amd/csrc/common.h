@@ -46,6 +46,13 @@ __device__ __forceinline__ void store_from_f32<float>(float* p, float v) { *p = 
 template <>
 __device__ __forceinline__ void store_from_f32<uint16_t>(uint16_t* p, float v) { *p = f32_to_bf16(v); }
 
+// Log-decays below this are taken as this: e^{-120} is zero in fp32 (and
+// e^{g} for g < -120 is below 1e-52 in any format), so the state is reset
+// exactly as the recurrence would; bounding g keeps the chunk-local
+// cumulative sums and their differences finite (g = -inf would give
+// -inf - -inf) and accurate.
+constexpr float kMinLogDecay = -120.f;
+
 // Reinterpret 8 raw bf16 words as the MFMA operand vector.
 __device__ __forceinline__ bf16x8 as_bf16x8(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
 

@@ -273,6 +273,7 @@ __global__ __launch_bounds__(kNT, 4) void chunk_prep_kernel(ChunkArgs a, unsigne
     }
     if (wave == 1) sm.bin[lane] = gv;
     if (wave == 0) {
+      gv = gv < kMinLogDecay ? kMinLogDecay : gv;  // (a NaN stays NaN)
       // chunk-local cumulative log-decay, summed in fp64 while the k/q loads
       // are in flight; kept as log2 (G * log2 e)
       double G = (double)gv;

@@ -89,7 +89,10 @@ __global__ __launch_bounds__(256) void chunk_f32_kernel(ChunkArgs a) {
     if (tid == 0) {
       double G = 0.0;
       for (int i = 0; i < C; ++i) {
-        if (i < L) G += (double)a.g[(size_t)(c0 + i) * Hv + h];
+        if (i < L) {
+          const float gi = a.g[(size_t)(c0 + i) * Hv + h];
+          G += (double)(gi < kMinLogDecay ? kMinLogDecay : gi);  // (a NaN stays NaN)
+        }
         sm.G[i] = G;
       }
     }

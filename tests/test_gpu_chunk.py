@@ -101,6 +101,33 @@ def test_nan_in_one_sequence_stays_there():
     assert torch.isnan(s2[1]).any()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_no_write_no_decay_keeps_state_bit_exact(dtype):
+    """beta = 0 and g = 0 (the degenerate case of the update): the final state is
+    the initial state bit for bit on both paths, and o = S0 q^ within tolerance."""
+    import torch
+    x = synth.gdr_inputs(44, B=1, T=200, dtype=dtype, initial_state_std=0.05)
+    x = synth.GDRInputs(x.q, x.k, x.v, np.zeros_like(x.g), np.zeros_like(x.beta), x.A_log, x.dt_bias, dtype, 64,
+                        x.initial_state)
+    say(f"chunk beta=0, g=0, {dtype}")
+    o, s = _check(x, s0=x.initial_state, tol=BF16_TOL if dtype == "bf16" else F32_TOL)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(s), x.initial_state)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_reset_by_infinite_decay(dtype):
+    """g = -inf (alpha = 0) on a few tokens, inside chunks and at a chunk start:
+    the state restarts from beta v k^T there (oracle: exact reset)."""
+    x = synth.gdr_inputs(45, B=1, T=300, dtype=dtype, initial_state_std=0.05)
+    g = x.g.copy()
+    g[0, [5, 64, 130, 131, 299], :] = -np.inf
+    g[0, 200, ::2] = -np.inf
+    x = synth.GDRInputs(x.q, x.k, x.v, g, x.beta, x.A_log, x.dt_bias, dtype, 64, x.initial_state)
+    say(f"chunk g=-inf resets, {dtype}")
+    _check(x, s0=x.initial_state, tol=BF16_TOL if dtype == "bf16" else F32_TOL)
+
+
 def test_chained_calls_equal_single_call_bit_exact():
     """Resume at chunk multiples: 4 x 256 chained calls == one 1024-token call."""
     import gated_delta_rule_amd as gdr_amd

@@ -111,3 +111,25 @@ def test_decode_deterministic_and_empty_batch():
     ef = torch.empty((0, 48), device=dev)
     es = torch.empty((0, 48, 128, 128), device=dev)
     assert gdr_amd.recurrent_step(e, e, ev, ef, ef, es).shape == (0, 48, 128)
+
+
+def test_decode_reset_and_no_write():
+    """g = -inf resets the state to beta v k^T; beta = 0 with g = 0 keeps it bit for bit."""
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    say("decode degenerate gates N=4")
+    A_log, dt, s0 = synth.decode_inputs(N=4)
+    x = synth.decode_step_inputs(2, N=4)
+    g = x.g.copy()
+    g[0] = -np.inf
+    g[1] = 0.0
+    beta = x.beta.copy()
+    beta[1] = 0.0
+    state = to_dev(s0, "f32", dev)
+    o = gdr_amd.recurrent_step(to_dev(x.q, "bf16", dev), to_dev(x.k, "bf16", dev), to_dev(x.v, "bf16", dev),
+                               to_dev(g, "f32", dev), to_dev(beta, "f32", dev), state)
+    torch.cuda.synchronize()
+    o_ref, s_ref = ref.decode_step(x.q, x.k, x.v, g, beta, s0.astype(np.float64))
+    assert rel_err(to_host(o), o_ref) <= BF16_TOL and rel_err(to_host(state), s_ref) <= BF16_TOL
+    assert np.array_equal(to_host(state)[1], s0[1])
