@@ -11,18 +11,26 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// bf16 <-> fp32 on raw bits.  Rounding is to nearest, ties to even; NaN is
-// kept quiet.
+// bf16 -> fp32 on raw bits (exact).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+// Round to nearest even with the hardware conversion (gfx950's packed
+// f32 -> bf16 convert: identical to integer round-to-nearest-even on every
+// non-NaN input, checked over all 2^32 bit patterns; a NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Two values rounded as above, packed low = a, high = b (one instruction).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t h;
+  h[0] = (__bf16)a;
+  h[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 // Split x into bf16 hi + lo with hi = rne(x), lo = rne(x - hi): hi + lo

@@ -52,11 +52,13 @@ constexpr int kXcds = 8;  // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kMatBytes = 6144;
 constexpr int kFacOff = 4 * kMatBytes;
 constexpr size_t kRecBytes = 25728;
-constexpr size_t kTableBytes(int N) { return (((size_t)N + 1) * 4 + 255) / 256 * 256; }
+// Workspace head: table[0..N] (chunk offsets of the sequences), then
+// order[0..N-1] (sequences by falling chunk count, the recurrence's launch
+// order).
+constexpr size_t kTableBytes(int N) { return (((size_t)N * 2 + 1) * 4 + 255) / 256 * 256; }
+constexpr int kOrderBins = 1024;  // chunk-count classes of the launch order
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Physical position of contraction index x in a 32-block: logical
 // x = 16*hi + 4*q + e lives at 8*q + 4*hi + e, so the 8 values lane group q
@@ -181,17 +183,25 @@ __device__ __forceinline__ ChunkPos locate_chunk(const ChunkArgs& a, const int32
 }
 
 // ---------------------------------------------------------------------------
-// Chunk table: table[n] = number of chunks of sequences 0..n-1.
+// Chunk table: table[n] = number of chunks of sequences 0..n-1, and
+// order[] = the sequences by falling chunk count (counts above
+// kOrderBins - 1 share one class; order inside a class is whatever the LDS
+// atomics give, which moves only the launch schedule, never a result).
 
 __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, int N, int32_t* table) {
   __shared__ int part[1024];
+  __shared__ int hist[kOrderBins];
   const int t = threadIdx.x;
   const int per = (N + 1023) / 1024;
   const int n0 = min(N, t * per), n1 = min(N, n0 + per);
+  auto nchunks = [&](int n) { return (cu[n + 1] - cu[n] + kC - 1) / kC; };
+  auto bin = [&](int n) { return min(nchunks(n), kOrderBins - 1); };
+  hist[t] = 0;
   int sum = 0;
-  for (int n = n0; n < n1; ++n) sum += (cu[n + 1] - cu[n] + kC - 1) / kC;
+  for (int n = n0; n < n1; ++n) sum += nchunks(n);
   part[t] = sum;
   __syncthreads();
+  for (int n = n0; n < n1; ++n) atomicAdd(&hist[bin(n)], 1);
   for (int off = 1; off < 1024; off <<= 1) {
     const int v = t >= off ? part[t - off] : 0;
     __syncthreads();
@@ -201,9 +211,25 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
   int run = t ? part[t - 1] : 0;
   for (int n = n0; n < n1; ++n) {
     table[n] = run;
-    run += (cu[n + 1] - cu[n] + kC - 1) / kC;
+    run += nchunks(n);
   }
   if (t == 1023) table[N] = part[1023];
+  // Start of class b in the order: sequences in classes above b.  Inclusive
+  // scan of the classes taken from the top: part[i] = sum of hist[1023 - i'],
+  // i' <= i.
+  __syncthreads();
+  part[t] = hist[kOrderBins - 1 - t];
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  hist[kOrderBins - 1 - t] = part[t] - hist[kOrderBins - 1 - t];  // exclusive start
+  __syncthreads();
+  int32_t* order = table + N + 1;
+  for (int n = n0; n < n1; ++n) order[atomicAdd(&hist[bin(n)], 1)] = n;
 }
 
 // ---------------------------------------------------------------------------
@@ -645,16 +671,21 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
   const int role = wv >> 1;  // 0 state, 1 output, 2 load
   const int wave = wv & 1;   // channel group of a state/output wave, or load wave index lw
   const int c = lane & 15, q4 = lane >> 4;
-  // Workgroup -> (sequence, value head, slice), XCD-aware: consecutive
-  // workgroup ids go round-robin to the 8 XCDs, each with its own L2, so the
-  // ids are renumbered to give every XCD a contiguous run of (key head, value
-  // head, slice) -- the workgroups that read the same k, q and chunk records
-  // then share one L2.
-  const int nslice = kD / kDVS, per_seq = a.Hv * nslice, total = a.N * per_seq;
-  int lin = blockIdx.x;
-  if (total % kXcds == 0) lin = (lin % kXcds) * (total / kXcds) + lin / kXcds;
-  const int n = lin / per_seq, slice = lin % nslice, h = (lin % per_seq) / nslice;
-  const int kh = h / (a.Hv / a.Hk);
+  // Workgroup -> (sequence, value head, slice).  A unit is the G workgroups
+  // of one (sequence, key head): every value head of the key head and every
+  // slice, all reading the same k and q.  Workgroup ids go round-robin to the
+  // 8 XCDs (each with its own L2), so id = 8 * (G * w + m) + x runs member m
+  // of the x-th unit of dispatch wave w on XCD x, and a unit never straddles
+  // two L2s.  Units go out longest sequence first (the table's order), which
+  // spreads a long sequence over every XCD and lets the short ones fill in
+  // behind it.
+  const int nslice = kD / kDVS, G = (a.Hv / a.Hk) * nslice;
+  const int xcd = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
+  const int u = (loc / G) * kXcds + xcd;
+  if (u >= a.N * a.Hk) return;
+  const int kh = u % a.Hk, m = loc % G;
+  const int n = a.cu_seqlens ? reinterpret_cast<const int32_t*>(ws)[a.N + 1 + u / a.Hk] : u / a.Hk;
+  const int h = kh * (a.Hv / a.Hk) + m / nslice, slice = m % nslice;
   const int vcol = slice * kDVS + 16 * wave + c;  // this lane's value channel
   int bos, eos, jb;
   if (a.cu_seqlens) {
@@ -959,7 +990,10 @@ hipError_t launch_rec_t(const ChunkArgs& a, const unsigned char* ws, hipStream_t
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((kD / kDVS) * a.Hv * a.N), dim3(kRecNT), smem, st, a, ws);
+  const int units = a.N * a.Hk, G = (a.Hv / a.Hk) * (kD / kDVS);
+  const unsigned grid = (unsigned)((units + kXcds - 1) / kXcds * kXcds * G);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kRecNT), smem, st, a, ws);
   return hipGetLastError();
 }
 

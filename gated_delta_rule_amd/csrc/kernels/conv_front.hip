@@ -8,11 +8,18 @@
 // acc = ((p0 + p1) + p2) + p3, y = acc / (1 + exp32(-acc)), rounded to nearest
 // even bf16, where exp32 is Cody and Waite's reduction x = n ln2 + r with
 // ln2 = C1 + C2, followed by the degree-7 Taylor polynomial of exp(r) in
-// Horner form and a scale by 2^n.  Every step is one IEEE fp32 operation; FMA
-// contraction is disabled below so that no two of them are fused.
+// Horner form and a scale by 2^n.  Every step of exp32 is one IEEE fp32
+// operation; FMA contraction is disabled below so that no two of them are
+// fused.
 //
-// HBM-bound: each thread owns 8 channels (16-byte loads) of a run of tokens
-// and slides a 3-token window through registers, so each input is read once.
+// Bound by the vector ALU, not by HBM: the contract costs about 40 fp32
+// instructions per element (the unfused Horner steps alone are 14), and
+// gfx950 retires 64 lanes of them per clock per compute unit.  Everything
+// else is cut to the bone: the division is replaced where that is exact
+// (silu32_mid), rounding uses the hardware conversion, and the special cases
+// cost no per-element compare.  Each thread owns 8 channels (16-byte loads) of
+// a run of 8 tokens and reads each of the run's 11 input rows (3 of history)
+// once; a run of 8 keeps the fully unrolled body in the instruction cache.
 #include "../common.h"
 #include "../internal.h"
 
@@ -23,12 +30,11 @@ namespace gdr {
 namespace {
 
 constexpr int kConvThreads = 256;
-constexpr int kConvRun = 16;  // tokens per thread
+constexpr int kConvRun = 8;  // tokens per thread
 
-__device__ __forceinline__ float exp32(float x) {
-  if (x != x) return x;
-  if (x > 0x1.62e430p+6f) return __builtin_inff();
-  if (x < -0x1.9fe368p+6f) return 0.f;
+// Cody-Waite reduction and the Taylor polynomial scaled by 2^n, with no
+// special cases (exp32 for x in [kExpLo, kExpHi]).
+__device__ __forceinline__ float exp_poly(float x) {
   const float n = __builtin_rintf(x * 0x1.715476p+0f);
   const float r = (x - n * 0x1.630000p-1f) - n * -0x1.bd0106p-13f;
   float p = 0x1.a01a02p-13f;
@@ -42,12 +48,29 @@ __device__ __forceinline__ float exp32(float x) {
   return __builtin_ldexpf(p, static_cast<int>(n));
 }
 
-__device__ __forceinline__ float silu32(float v) { return v / (1.0f + exp32(-v)); }
+// exp32 is +inf above kExpHi = 0x1.62e430p+6 (about 88.72) and 0 below kExpLo.
+constexpr float kExpLo = -0x1.9fe368p+6f;
 
-__device__ __forceinline__ void load8(const uint16_t* p, float* out) {
-  const u16x8 raw = *reinterpret_cast<const u16x8*>(p);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) out[j] = bf16_to_f32(raw[j]);
+// SiLU by the contract for every v.  exp32(-v) is taken as exp_poly on -v
+// clamped into [kExpLo, 128], which gives the same quotient: above kExpHi the
+// scale by 2^n overflows to +inf for every x up to 128, as exp32 does; below
+// kExpLo the clamped value is at most 2^-149, so 1 + e rounds to 1, as it does
+// for exp32's 0; a NaN v stays NaN through the division.
+__device__ __forceinline__ float silu32(float v) {
+  return v / (1.0f + exp_poly(fminf(fmaxf(-v, kExpLo), 128.f)));
+}
+
+// SiLU for |v| <= 80, where no clamp is needed and the IEEE division can be
+// replaced by one residual correction of v * rcp(d): q0 = v y0, r = d q0 - v
+// (exact by the fused multiply-add), q = q0 - r y0.  The residual is taken
+// as d q0 - v rather than v - d q0 so that v = -0 keeps its sign.  Checked
+// equal, bit for bit, to silu32 for every fp32 v in [-80, 80].
+__device__ __forceinline__ float silu32_mid(float v) {
+  const float d = 1.0f + exp_poly(-v);
+  const float y0 = __builtin_amdgcn_rcpf(d);
+  const float q0 = v * y0;
+  const float rn = __builtin_fmaf(d, q0, -v);
+  return __builtin_fmaf(-rn, y0, q0);
 }
 
 // Sequence index n with cu[n] <= t < cu[n+1] (empty sequences skipped).
@@ -60,42 +83,34 @@ __device__ __forceinline__ int seq_of(const int32_t* cu, int N, int t) {
   return lo;
 }
 
-__global__ __launch_bounds__(kConvThreads) void conv_front_kernel(ConvArgs a) {
+// Conv + SiLU of channels cg*8 .. +7 over tokens t0 .. t0+7.  The run's 11
+// input rows (3 of history; indexes clamped into [0, T), the clamped ones
+// never used) are loaded before anything else, the sequence lookup included.
+__device__ __forceinline__ void conv_run(const ConvArgs& a, int cg, int t0) {
   const int C = (2 * a.Hk + a.Hv) * a.D;
   const int Cq = a.Hk * a.D;
-  const int t0 = blockIdx.y * kConvRun;
-  const int t_end = min(t0 + kConvRun, a.T);
-
-  // Gates for this token run, one workgroup column per run.
-  if (blockIdx.x == 0) {
-    for (int e = threadIdx.x; e < kConvRun * a.Hv; e += kConvThreads) {
-      const int t = t0 + e / a.Hv, hh = e % a.Hv;
-      if (t < a.T) {
-        const size_t i = (size_t)t * a.Hv + hh;
-        const float x = a.a[i] + a.dt_bias[hh];
-        const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-        a.g[i] = -expf(a.A_log[hh]) * sp;
-        a.beta[i] = 1.f / (1.f + expf(-a.b[i]));
-      }
-    }
-  }
-
-  const int cg = blockIdx.x * kConvThreads + threadIdx.x;
   if (cg * 8 >= C || t0 >= a.T) return;
   const int c0 = cg * 8;
   const uint16_t* x = static_cast<const uint16_t*>(a.x);
   const uint16_t* sin = static_cast<const uint16_t*>(a.state_in);
+
+  u16x8 raw[kConvRun + 3];  // raw[i]: input row t0 - 3 + i
+#pragma unroll
+  for (int i = 0; i < kConvRun + 3; ++i) {
+    const int r = min(max(t0 - 3 + i, 0), a.T - 1);
+    raw[i] = *reinterpret_cast<const u16x8*>(x + (size_t)r * C + c0);
+  }
 
   float w[4][8];
   {
     const u16x8* wp = reinterpret_cast<const u16x8*>(static_cast<const uint16_t*>(a.w) + (size_t)c0 * 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const u16x8 raw = wp[q];  // channels c0 + 2q, c0 + 2q + 1, taps 0..3 each
+      const u16x8 rw = wp[q];  // channels c0 + 2q, c0 + 2q + 1, taps 0..3 each
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        w[j][2 * q] = bf16_to_f32(raw[j]);
-        w[j][2 * q + 1] = bf16_to_f32(raw[4 + j]);
+        w[j][2 * q] = bf16_to_f32(rw[j]);
+        w[j][2 * q + 1] = bf16_to_f32(rw[4 + j]);
       }
     }
   }
@@ -112,24 +127,23 @@ __global__ __launch_bounds__(kConvThreads) void conv_front_kernel(ConvArgs a) {
 
   int n = seq_of(a.cu_seqlens, a.N, t0);
   int bos = a.cu_seqlens[n], eos = a.cu_seqlens[n + 1];
+  // History of token t0: inputs of the same sequence, else the carried conv
+  // state (oldest first), else zero.
   float h[3][8];
-  // History of the token before t0: inputs of the same sequence, else the
-  // carried conv state (oldest first), else zero.
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const int p = t0 - 3 + j;
-    if (p >= bos) {
-      load8(x + (size_t)p * C + c0, h[j]);
-    } else if (sin) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) h[j][c] = bf16_to_f32(sin[((size_t)n * C + c0 + c) * 3 + (p - bos + 3)]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) h[j][c] = 0.f;
-    }
+    for (int c = 0; c < 8; ++c)
+      h[j][c] = p >= bos ? bf16_to_f32(raw[j][c])
+              : sin      ? bf16_to_f32(sin[((size_t)n * C + c0 + c) * 3 + (p - bos + 3)])
+                         : 0.f;
   }
 
-  for (int t = t0; t < t_end; ++t) {
+#pragma unroll
+  for (int i = 0; i < kConvRun; ++i) {
+    const int t = t0 + i;
+    if (t >= a.T) break;
     if (t >= eos) {  // a new sequence starts at t
       while (a.cu_seqlens[n + 1] <= t) ++n;
       bos = a.cu_seqlens[n];
@@ -140,21 +154,51 @@ __global__ __launch_bounds__(kConvThreads) void conv_front_kernel(ConvArgs a) {
         for (int c = 0; c < 8; ++c)
           h[j][c] = sin ? bf16_to_f32(sin[((size_t)n * C + c0 + c) * 3 + j]) : 0.f;
     }
-    float xt[8];
-    load8(x + (size_t)t * C + c0, xt);
-    u16x8 y;
+    float acc[8];
+    bool mid = true;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      float acc = w[0][c] * h[0][c];
-      acc = acc + w[1][c] * h[1][c];
-      acc = acc + w[2][c] * h[2][c];
-      acc = acc + w[3][c] * xt[c];
-      y[c] = f32_to_bf16(silu32(acc));
+      const float xt = bf16_to_f32(raw[i + 3][c]);
+      float s = w[0][c] * h[0][c];
+      s = s + w[1][c] * h[1][c];
+      s = s + w[2][c] * h[2][c];
+      s = s + w[3][c] * xt;
+      acc[c] = s;
+      mid = mid && fabsf(s) <= 80.f;
       h[0][c] = h[1][c];
       h[1][c] = h[2][c];
-      h[2][c] = xt[c];
+      h[2][c] = xt;
     }
-    *reinterpret_cast<u16x8*>(out + (size_t)t * ld + col) = y;
+    // One wave-wide test per token: the general path runs only when some
+    // lane's pre-activation leaves [-80, 80] (or is NaN).
+    if (__all(mid)) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = silu32_mid(acc[c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = silu32(acc[c]);
+    }
+    u32x4 y;
+#pragma unroll
+    for (int c = 0; c < 8; c += 2) y[c / 2] = pack_bf16x2(acc[c], acc[c + 1]);
+    *reinterpret_cast<u32x4*>(out + (size_t)t * ld + col) = y;
+  }
+}
+
+__global__ __launch_bounds__(kConvThreads) void conv_front_kernel(ConvArgs a) {
+  const int t0 = blockIdx.y * kConvRun;
+  conv_run(a, blockIdx.x * kConvThreads + threadIdx.x, t0);
+  // Gates of this token run, spread over the run's workgroups, after the
+  // conv so that its row loads go out first.
+  for (int e = blockIdx.x * kConvThreads + threadIdx.x; e < kConvRun * a.Hv; e += gridDim.x * kConvThreads) {
+    const int t = t0 + e / a.Hv, hh = e % a.Hv;
+    if (t < a.T) {
+      const size_t i = (size_t)t * a.Hv + hh;
+      const float x = a.a[i] + a.dt_bias[hh];
+      const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+      a.g[i] = -expf(a.A_log[hh]) * sp;
+      a.beta[i] = 1.f / (1.f + expf(-a.b[i]));
+    }
   }
 }
 

@@ -4,7 +4,7 @@
 // parameter ledger: the gate z is Hv * d_v = 6144 wide).
 //
 // HBM-bound streaming kernel: d_v/4 lanes per row, 16-byte o loads, one
-// reduction per row, bf16 output.
+// reduction per row, bf16 output; four rows per thread in flight.
 #include "../common.h"
 #include "../internal.h"
 
@@ -12,35 +12,57 @@ namespace gdr {
 
 namespace {
 
+// Each thread takes kNormUnroll rows per pass and issues all their loads
+// before the first reduction, so several rows of o and z are in flight.
+constexpr int kNormUnroll = 4;
+
 template <int D, typename TO>
 __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(const TO* __restrict__ o,
                                                             const uint16_t* __restrict__ z,
                                                             const float* __restrict__ w,
                                                             uint16_t* __restrict__ y, int rows, float eps) {
   constexpr int LPR = D / 4;
-  constexpr int RPB = 256 / LPR;  // rows per workgroup per iteration
+  constexpr int RPB = 256 / LPR;  // rows per workgroup per unrolled step
   const int sub = threadIdx.x / LPR, c4 = threadIdx.x % LPR;
   float wv[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) wv[j] = w[4 * c4 + j];
-  for (int row = blockIdx.x * RPB + sub; row < rows; row += gridDim.x * RPB) {
-    float ov[4], zv[4];
-    const TO* op = o + (size_t)row * D + 4 * c4;
+  for (int base = blockIdx.x * RPB * kNormUnroll; base < rows; base += gridDim.x * RPB * kNormUnroll) {
+    float ov[kNormUnroll][4], zv[kNormUnroll][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) ov[j] = load_as_f32(op + j);
-    const u16x4 zr = *reinterpret_cast<const u16x4*>(z + (size_t)row * D + 4 * c4);
+    for (int u = 0; u < kNormUnroll; ++u) {
+      const int row = base + u * RPB + sub;
+      if (row < rows) {
+        const TO* op = o + (size_t)row * D + 4 * c4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) zv[j] = bf16_to_f32(zr[j]);
-    float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
-    ss = group_sum<LPR>(ss);
-    const float rstd = 1.f / sqrtf(ss / D + eps);
-    u16x4 out;
+        for (int j = 0; j < 4; ++j) ov[u][j] = load_as_f32(op + j);
+        const u16x4 zr = *reinterpret_cast<const u16x4*>(z + (size_t)row * D + 4 * c4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float gate = zv[j] / (1.f + expf(-zv[j]));
-      out[j] = f32_to_bf16(ov[j] * rstd * wv[j] * gate);
+        for (int j = 0; j < 4; ++j) zv[u][j] = bf16_to_f32(zr[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ov[u][j] = zv[u][j] = 0.f;
+      }
     }
-    *reinterpret_cast<u16x4*>(y + (size_t)row * D + 4 * c4) = out;
+#pragma unroll
+    for (int u = 0; u < kNormUnroll; ++u) {
+      const int row = base + u * RPB + sub;
+      float ss = ov[u][0] * ov[u][0] + ov[u][1] * ov[u][1] + ov[u][2] * ov[u][2] + ov[u][3] * ov[u][3];
+      ss = group_sum<LPR>(ss);
+      const float rstd = 1.f / sqrtf(ss / D + eps);
+      float yv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // z sigmoid(z) with the hardware exp2 and reciprocal (about 1e-7
+        // relative, far inside a bf16 ulp): z = -inf gives NaN, z = +inf
+        // gives +inf, as z / (1 + e^-z) does.
+        const float e = __builtin_amdgcn_exp2f(zv[u][j] * -1.44269504f);
+        const float gate = zv[u][j] * __builtin_amdgcn_rcpf(1.f + e);
+        yv[j] = ov[u][j] * rstd * wv[j] * gate;
+      }
+      if (row < rows)
+        *reinterpret_cast<u32x2*>(y + (size_t)row * D + 4 * c4) = u32x2{pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3])};
+    }
   }
 }
 
@@ -48,7 +70,7 @@ template <int D>
 hipError_t launch_norm_d(const NormArgs& a, hipStream_t st) {
   const int rows = a.T * a.H;
   constexpr int RPB = 256 / (D / 4);
-  int blocks = (rows + RPB - 1) / RPB;
+  int blocks = (rows + RPB * kNormUnroll - 1) / (RPB * kNormUnroll);
   if (blocks > 8192) blocks = 8192;
   if (a.o_bf16)
     hipLaunchKernelGGL((gated_rmsnorm_kernel<D, uint16_t>), dim3(blocks), dim3(256), 0, st,

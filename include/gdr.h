@@ -101,7 +101,8 @@ const char* gdr_last_error(void);
 /*
  * Device workspace that gdr_chunk_fwd needs for descriptor *d, in bytes.
  * The bf16-MFMA path (bf16 q/k/v, d = 128, chunk 64) stores a chunk table
- * (N+1 int32, padded to 256 bytes) and one 25728-byte record per (chunk,
+ * and launch order (2N+1 int32, padded to 256 bytes) and one 25728-byte
+ * record per (chunk,
  * value head) -- the chunk's T = (I+A)^{-1} and P as bf16 hi/lo pairs and its
  * per-token factors -- for an upper bound of ceil(T/64) + N chunks when
  * batch == 1 (packed or single sequence) and B * ceil(T/64) otherwise.  Every

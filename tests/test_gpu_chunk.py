@@ -84,6 +84,20 @@ def test_varlen_packed_equals_separate_bit_exact():
         assert bits_equal(s[n:n + 1], sn)
 
 
+def test_varlen_many_sequences_launch_order():
+    """1031 sequences: more than one per thread of the chunk-table kernel,
+    empty ones, and one of 1032 chunks (past the top class of the
+    longest-first launch order).  Every (sequence, head, slice) must run once."""
+    rng = np.random.default_rng(26)
+    lens = list(rng.integers(0, 40, size=1030))
+    lens.insert(500, 66000)
+    cu = synth.cu_seqlens_of(lens)
+    x = synth.gdr_inputs(27, B=1, T=int(cu[-1]), hk=1, hv=2, d=128, dtype="bf16")
+    s0 = (0.05 * np.random.default_rng(28).standard_normal((len(lens), 2, 128, 128))).astype(np.float32)
+    say(f"chunk varlen {len(lens)} sequences, {int(cu[-1])} tokens")
+    _check(x, cu=cu, s0=s0)
+
+
 def test_nan_in_one_sequence_stays_there():
     import torch
     lens = [100, 90, 80]

@@ -53,6 +53,32 @@ def test_conv_bit_exact_small(lens):
     assert np.max(np.abs(to_host(beta)[0] - b_ref) / b_ref) < 2e-6
 
 
+def test_conv_every_bf16_input_bit_exact():
+    """SiLU's general and |acc| <= 80 paths and the special values: 64 channels
+    each run through all 65536 bf16 bit patterns (infinities, NaN, subnormals,
+    the overflow range) in their own order, 64 more with pre-activations spread
+    across +-80; bit for bit, NaN matched by position."""
+    dev = gpu()
+    T, C = 65536, 128
+    p = synth.pipeline_inputs(seed=30, lengths=[T // 2, T // 2], hk=1, hv=2, d=32)
+    rng = np.random.default_rng(31)
+    pats = np.arange(65536, dtype=np.uint32) << 16
+    x = np.empty((T, C), np.float32)
+    for c in range(64):
+        x[:, c] = rng.permutation(pats).view(np.float32)
+    x[:, 64:] = synth.round_bf16(60.0 * rng.standard_normal((T, 64)))
+    p = synth.PipelineInputs(x, p.conv_w, p.a, p.b, p.A_log, p.dt_bias, p.z, p.norm_w, p.cu_seqlens,
+                             p.hk, p.hv, p.d)
+    say("conv SiLU sweep: all bf16 inputs")
+    y = _y_of(*_front(p, dev)[:3])
+    with np.errstate(over="ignore", invalid="ignore"):
+        y_ref = cref.conv_silu_fp32(p.x, p.conv_w, p.cu_seqlens)
+    got = to_host(y.float())
+    nan = np.isnan(y_ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(_bits(y)[~nan], _bits_np(y_ref)[~nan])
+
+
 def test_conv_state_carry_bit_exact():
     """Conv over a sequence in pieces, carrying conv_state, equals one pass."""
     dev = gpu()
