@@ -11,14 +11,44 @@
 //
 // which is S_t = alpha S (I - beta k k^T) + beta v k^T, o = S_t q multiplied
 // out.  The whole update is HBM-bound (0.875 FLOP per state byte), so the
-// kernel is organised for streaming: one workgroup per state, every lane
-// issues all of its 16-byte state loads before reducing, rows are read as
-// contiguous 512-byte runs by 32 lanes, and the state is written back from the
-// same registers.
+// kernel is organised for streaming: one or two workgroups per state, every
+// lane issues all of its 16-byte state loads before reducing, and the state
+// is written back from the same registers.  State loads and stores are
+// non-temporal: a pool of states is read once and written once per token and
+// in a real model (dozens of layers) never fits the 256 MB last-level cache,
+// so they stream past it; measured, this gives the same rate whether or not
+// the state would have fit there.  Eight lanes share a state row: lane
+// e (0..7) holds columns 32 j + 4 e .. +3 for j < D/32, so every load
+// instruction reads 128 contiguous bytes of each of its 8 rows, and a row's
+// dot products finish with three cross-lane adds inside the 8-lane group
+// (data-parallel-primitive moves, no LDS traffic).
 #include "../common.h"
 #include "../internal.h"
 
 namespace gdr {
+
+namespace {
+
+// Sum over the 8-lane group (lanes 8m .. 8m+7); every lane gets the same
+// value (each step adds a lane pair in both orders).
+// Workgroups per state: at d = 128 two, each streaming 64 of the 128 rows,
+// so that a lane holds 32 state registers and more workgroups share a
+// compute unit (every state row is independent given k, q, v and the gates).
+template <int D>
+constexpr int kDecodeSplit = D == 128 ? 2 : 1;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp_move<0x141>(x);  // row_half_mirror: lane i <-> 7 - i of its 8
+  return x;
+}
+
+}  // namespace
 
 template <int D, typename TQ, typename TO>
 __global__ __launch_bounds__(256) void decode_kernel(const TQ* __restrict__ q, const TQ* __restrict__ k,
@@ -26,52 +56,60 @@ __global__ __launch_bounds__(256) void decode_kernel(const TQ* __restrict__ q, c
                                                      const float* __restrict__ beta, float* __restrict__ state,
                                                      TO* __restrict__ o, int Hk, int Hv, int use_l2,
                                                      float scale, float eps) {
-  constexpr int LPR = D / 4;         // lanes per state row (4 floats each)
-  constexpr int RPS = 64 / LPR;      // rows per wave per step
-  constexpr int NS = (D / 4) / RPS;  // steps per wave (each wave owns D/4 rows)
-  const int nh = blockIdx.x;
+  constexpr int F4 = D / 32;                 // 16-byte pieces per lane per row
+  constexpr int SPLIT = kDecodeSplit<D>;     // workgroups per state
+  constexpr int NS = D / (32 * SPLIT);       // row steps per wave, 8 rows each
+  const int nh = blockIdx.x / SPLIT, part = blockIdx.x % SPLIT;
   const int n = nh / Hv, h = nh - n * Hv;
   const int kh = h / (Hv / Hk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane / LPR, c4 = lane % LPR;
+  const int sub = lane >> 3, e8 = lane & 7;
 
   float* S = state + (size_t)nh * D * D;
-  const int row0 = wave * (D / 4) + sub;
+  const int row0 = part * (D / SPLIT) + wave * (D / (4 * SPLIT)) + sub;
 
-  // Issue every state load first: 16 x 16 B per lane in flight for D = 128.
-  f32x4 s[NS];
+  // Issue every state load first: NS * F4 x 16 B per lane in flight.
+  f32x4 s[NS][F4];
 #pragma unroll
   for (int i = 0; i < NS; ++i)
-    s[i] = *reinterpret_cast<const f32x4*>(S + (size_t)(row0 + i * RPS) * D + 4 * c4);
-
-  float kv[4], qv[4];
-  const TQ* kp = k + ((size_t)n * Hk + kh) * D + 4 * c4;
-  const TQ* qp = q + ((size_t)n * Hk + kh) * D + 4 * c4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    kv[j] = load_as_f32(kp + j);
-    qv[j] = load_as_f32(qp + j);
-  }
+    for (int j = 0; j < F4; ++j)
+      s[i][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(row0 + 8 * i) * D + 32 * j + 4 * e8));
+
+  float kv[F4][4], qv[F4][4];
+  const TQ* kp = k + ((size_t)n * Hk + kh) * D + 4 * e8;
+  const TQ* qp = q + ((size_t)n * Hk + kh) * D + 4 * e8;
+#pragma unroll
+  for (int j = 0; j < F4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kv[j][e] = load_as_f32(kp + 32 * j + e);
+      qv[j][e] = load_as_f32(qp + 32 * j + e);
+    }
   float kk = 0.f, qq = 0.f, kq = 0.f;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    kk += kv[j] * kv[j];
-    qq += qv[j] * qv[j];
-    kq += kv[j] * qv[j];
-  }
-  kk = group_sum<LPR>(kk);
-  qq = group_sum<LPR>(qq);
-  kq = group_sum<LPR>(kq);
+  for (int j = 0; j < F4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kk += kv[j][e] * kv[j][e];
+      qq += qv[j][e] * qv[j][e];
+      kq += kv[j][e] * qv[j][e];
+    }
+  kk = sum8(kk);
+  qq = sum8(qq);
+  kq = sum8(kq);
   float rk = 1.f, rq = 1.f;
   if (use_l2) {
     rk = 1.f / sqrtf(kk + eps);
     rq = 1.f / sqrtf(qq + eps);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    kv[j] *= rk;
-    qv[j] *= rq;
-  }
+  for (int j = 0; j < F4; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kv[j][e] *= rk;
+      qv[j][e] *= rq;
+    }
   kq *= rk * rq;
 
   const float alpha = expf(g[nh]);
@@ -81,25 +119,32 @@ __global__ __launch_bounds__(256) void decode_kernel(const TQ* __restrict__ q, c
 
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    const int r = row0 + i * RPS;
-    float pu = s[i].x * kv[0] + s[i].y * kv[1] + s[i].z * kv[2] + s[i].w * kv[3];
-    float pw = s[i].x * qv[0] + s[i].y * qv[1] + s[i].z * qv[2] + s[i].w * qv[3];
-    pu = group_sum<LPR>(pu);
-    pw = group_sum<LPR>(pw);
+    const int r = row0 + 8 * i;
+    float pu = 0.f, pw = 0.f;
+#pragma unroll
+    for (int j = 0; j < F4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pu += s[i][j][e] * kv[j][e];
+        pw += s[i][j][e] * qv[j][e];
+      }
+    pu = sum8(pu);
+    pw = sum8(pw);
     const float delta = b * (load_as_f32(vp + r) - alpha * pu);
-    if (c4 == 0) store_from_f32(op + r, scale * (alpha * pw + delta * kq));
-    f32x4 ns;
-    ns.x = alpha * s[i].x + delta * kv[0];
-    ns.y = alpha * s[i].y + delta * kv[1];
-    ns.z = alpha * s[i].z + delta * kv[2];
-    ns.w = alpha * s[i].w + delta * kv[3];
-    *reinterpret_cast<f32x4*>(S + (size_t)r * D + 4 * c4) = ns;
+    if (e8 == 0) store_from_f32(op + r, scale * (alpha * pw + delta * kq));
+#pragma unroll
+    for (int j = 0; j < F4; ++j) {
+      f32x4 ns;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ns[e] = alpha * s[i][j][e] + delta * kv[j][e];
+      __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + (size_t)r * D + 32 * j + 4 * e8));
+    }
   }
 }
 
 template <int D, typename TQ, typename TO>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_kernel<D, TQ, TO>), dim3(a.N * a.Hv), dim3(256), 0, st,
+  hipLaunchKernelGGL((decode_kernel<D, TQ, TO>), dim3(a.N * a.Hv * kDecodeSplit<D>), dim3(256), 0, st,
                      static_cast<const TQ*>(a.q), static_cast<const TQ*>(a.k), static_cast<const TQ*>(a.v),
                      a.g, a.beta, a.state, static_cast<TO*>(a.o), a.Hk, a.Hv, a.use_l2, a.scale, a.eps);
   return hipGetLastError();

@@ -198,6 +198,51 @@ def test_two_stages_equal_one_call_bit_exact(dtype):
     assert bits_equal(o1, o2) and bits_equal(s1, s2)
 
 
+@pytest.mark.parametrize("T,hk,hv,mode", [(8192, 16, 48, "f32"), (3 * 4096 + 77, 2, 6, "f32"),
+                                          (3 * 4096 + 77, 2, 6, "inplace"), (2 * 4096 + 1, 16, 48, "nostate"),
+                                          (9000, 16, 48, "bf16out")])
+def test_long_single_sequence_equals_stagewise(T, hk, hv, mode):
+    """One long sequence (ragged tails included) through gdr_chunk_fwd equals
+    gdr_chunk_fwd_prepare + gdr_chunk_fwd_recurrence bit for bit (outputs and
+    final state), with the state in place, absent, and with bf16 outputs; and
+    matches the oracle."""
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    x = synth.gdr_inputs(60 + T % 97, B=1, T=T, hk=hk, hv=hv, dtype="bf16",
+                         initial_state_std=None if mode == "nostate" else 0.05)
+    say(f"chunk long single sequence T={T} heads {hk}/{hv} {mode}")
+    a = _dev_inputs(x, dev, s0=x.initial_state)
+    args = (a["q"], a["k"], a["v"], a["g"], a["beta"])
+    odt = torch.bfloat16 if mode == "bf16out" else torch.float32
+    s_in = a["initial_state"]
+    if mode == "inplace":
+        s1 = s_in.clone()
+        o1, _ = gdr_amd.chunk_gated_delta_rule(*args, s1, final_state=s1, out_dtype=odt)
+    elif mode == "nostate":
+        o1, s1 = gdr_amd.chunk_gated_delta_rule(*args, None, out_dtype=odt), None
+        o1 = o1[0]
+    else:
+        o1, s1 = gdr_amd.chunk_gated_delta_rule(*args, s_in, output_final_state=True, out_dtype=odt)
+    ws = gdr_amd.chunk_workspace(a["q"], a["v"])
+    o2 = torch.empty_like(o1)
+    s2 = torch.empty((1, hv, 128, 128), device=dev)
+    for stage in ("prepare", "recurrence"):
+        gdr_amd.chunk_gated_delta_rule(*args, s_in, final_state=s2, out=o2, workspace=ws, stage=stage,
+                                       out_dtype=odt)
+    torch.cuda.synchronize()
+    assert bits_equal(o1, o2)
+    if s1 is not None:
+        assert bits_equal(s1, s2)
+    if hv <= 6 or T <= 8192:
+        heads = list(range(hv)) if hv <= 6 else [0, 23, 47]
+        o_ref, s_ref = ref.forward(x.q, x.k, x.v, x.g, x.beta, x.initial_state, None, heads=heads)
+        eo = rel_err(to_host(o2)[:, :, heads], o_ref[:, :, heads])
+        es = rel_err(to_host(s2)[:, heads], s_ref[:, heads])
+        say(f"  o err {eo:.2e}  state err {es:.2e}")
+        assert eo <= BF16_TOL and es <= BF16_TOL
+
+
 @pytest.mark.parametrize("d,dtype,C", [(64, "bf16", 64), (64, "f32", 64), (128, "f32", 64), (128, "bf16", 32),
                                        (32, "bf16", 32)])
 def test_other_shapes_fp32_path(d, dtype, C):
