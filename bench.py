@@ -3,10 +3,11 @@
 
 A step is one 32768-token chunked-prefill call of one delta layer
 (16 key / 48 value heads, d = 128, bf16 q/k/v, fp32 gates, state and output,
-chunk 64) that resumes from the previous call's final state -- the shape of
-one call of a 262144-token context processed in 32K pieces.  ``value`` is the
-prefill rate in tokens/s over the K timed steps.  The same JSON line also
-reports, measured in the same run:
+chunk 64) that resumes from the previous call's final state.  The calls are
+the 8 consecutive pieces of one 262144-token context (distinct inputs, all
+resident in HBM); step s runs piece s % 8.  ``value`` is the prefill rate in
+tokens/s over the K timed steps.  The same JSON line also reports, measured
+in the same run:
 
   decode    -- 64 sequences x 48 heads of 128x128 fp32 state, one token per
                step, state updated in place, 256 steps: state GB/s
@@ -19,11 +20,16 @@ reports, measured in the same run:
                each recurrence launch inside the timed loop), against the
                8 TB/s HBM peak; plus its MFMA fraction and the HBM bytes the
                committed rocprofv3 counters measured for it
+  achievable -- the roofline probes (libgdr_roofline.so): streaming HBM
+               read-modify-write and read rates and the dense bf16 matrix-core
+               rate this GPU delivers, beside the datasheet peaks
+  clocks    -- rocm-smi's clock report before and after the run
   cpu_baseline -- the fp64 CPU oracle timed on the host cores on a bounded
-               sample of the same workload (the first three 32K-token calls)
+               sample of the same workload (the first three 32K-token calls;
+               and 4 decode steps for the decode leg)
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill|decode|pipeline|copy|all]
-                       [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pieces P] [--no-cpu]
+                       [--only prefill|decode|pipeline|copy|roofline|all]
 """
 from __future__ import annotations
 
@@ -43,6 +49,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 HK, HV, D, C = 16, 48, 128, 64
 T_CALL = 32768
+N_CALLS = 8  # pieces of the 262144-token context
 
 # Algorithmic bytes per prefill token: q, k (2*Hk*d bf16) + v (Hv*d bf16)
 # + g, beta (2*Hv fp32) + o (Hv*d fp32); per call add one read and one write
@@ -72,43 +79,49 @@ def _events():
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def bench_prefill(steps: int, warmup: int):
+def long_context_host(n: int = N_CALLS):
+    """The n calls' host inputs, generated in parallel threads (numpy releases
+    the GIL in the heavy parts)."""
+    import concurrent.futures as cf
+    from gated_delta_rule_amd import synth
+    workers = max(1, min(n, len(os.sched_getaffinity(0)) // 2))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(lambda i: synth.long_context_call(i, T=T_CALL), range(n)))
+
+
+def bench_prefill(steps: int, warmup: int, host_calls):
     import torch
     import gated_delta_rule_amd as gdr
-    from gated_delta_rule_amd import synth
     dev = torch.device("cuda:0")
-    log(f"prefill: generating T={T_CALL} inputs")
-    x = synth.long_context_call(0, T=T_CALL)
     bf = lambda a: torch.from_numpy(a).to(torch.bfloat16).to(dev)
     f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
-    q, k, v = bf(x.q), bf(x.k), bf(x.v)
-    g, beta = f32(x.g), f32(x.beta)
+    calls = [(bf(x.q), bf(x.k), bf(x.v), f32(x.g), f32(x.beta)) for x in host_calls]
     state = torch.zeros((1, HV, D, D), device=dev)
     o = torch.empty((1, T_CALL, HV, D), device=dev)
-    ws = gdr.chunk_workspace(q, v)
-    del x
+    ws = gdr.chunk_workspace(calls[0][0], calls[0][2])
 
     # One call = gdr_chunk_fwd_prepare + gdr_chunk_fwd_recurrence on the torch
     # stream (the same kernels gdr_chunk_fwd enqueues), so that events can
     # bracket the recurrence kernel alone.
-    def stage(name):
+    def stage(i, name):
+        q, k, v, g, beta = calls[i % N_CALLS]
         gdr.chunk_gated_delta_rule(q, k, v, g, beta, state, final_state=state, out=o, workspace=ws, stage=name)
 
-    log(f"prefill: {warmup} warmup + {steps} timed 32K calls")
-    for _ in range(warmup):
-        stage("prepare")
-        stage("recurrence")
+    log(f"prefill: {warmup} warmup + {steps} timed 32K calls over {N_CALLS} distinct pieces")
+    for i in range(warmup):
+        stage(i, "prepare")
+        stage(i, "recurrence")
     torch.cuda.synchronize()
     per = []
     t0 = time.perf_counter()
     start, end = _events()
     start.record()
-    for _ in range(steps):
+    for i in range(steps):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         e[0].record()
-        stage("prepare")
+        stage(warmup + i, "prepare")
         e[1].record()
-        stage("recurrence")
+        stage(warmup + i, "recurrence")
         e[2].record()
         per.append(e)
     end.record()
@@ -117,8 +130,58 @@ def bench_prefill(steps: int, warmup: int):
     total_ms = start.elapsed_time(end)
     prep_ms = [e[0].elapsed_time(e[1]) for e in per]
     recur_ms = [e[1].elapsed_time(e[2]) for e in per]
+    call_ms = [e[0].elapsed_time(e[2]) for e in per]
     finite = bool(torch.isfinite(state).all() and torch.isfinite(o).all())
-    return dict(total_ms=total_ms, wall_s=wall, prep_ms=prep_ms, recur_ms=recur_ms, finite=finite)
+    return dict(total_ms=total_ms, wall_s=wall, prep_ms=prep_ms, recur_ms=recur_ms, call_ms=call_ms, finite=finite)
+
+
+def bench_roofline(reps: int = 10):
+    """Achievable rates of this GPU from the roofline probes."""
+    import torch
+    from gated_delta_rule_amd import roofline
+    dev = torch.device("cuda:0")
+    nbytes = 2 << 30  # 2 GiB: well past the 256 MB last-level cache
+    buf = torch.ones(nbytes // 4, device=dev)
+    sums = torch.empty(nbytes // roofline.SLAB, device=dev)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        start, end = _events()
+        start.record()
+        for _ in range(reps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / reps
+
+    rmw_nt = 2 * nbytes / (timed(lambda: roofline.rmw(buf, 1.0, True)) * 1e-3) / 1e9
+    rmw = 2 * nbytes / (timed(lambda: roofline.rmw(buf, 1.0, False)) * 1e-3) / 1e9
+    rd = nbytes / (timed(lambda: roofline.read(buf, sums)) * 1e-3) / 1e9
+    del buf, sums
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs, iters = 8 * cus, 4000
+    out = torch.empty(wgs * 4, device=dev)
+    flop = wgs * 4 * iters * roofline.MFMA_FLOP_PER_WAVE_ITER
+    mfma = flop / (timed(lambda: roofline.mfma(out, wgs, iters)) * 1e-3) / 1e12
+    log(f"roofline probes: rmw nt {rmw_nt:.0f} GB/s, rmw {rmw:.0f} GB/s, read {rd:.0f} GB/s, mfma {mfma:.0f} TFLOP/s")
+    return {"hbm_rmw_nontemporal_GBps": rmw_nt, "hbm_rmw_GBps": rmw, "hbm_read_GBps": rd,
+            "mfma_bf16_TFLOPs": mfma, "buffer_bytes": nbytes}
+
+
+def gpu_clocks():
+    """rocm-smi's current clocks (text), or None if it cannot be read."""
+    import shutil
+    import subprocess
+    exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
+    if not exe:
+        return None
+    try:
+        r = subprocess.run([exe, "--showclocks"], capture_output=True, text=True, timeout=30)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    lines = [ln.strip() for ln in r.stdout.splitlines() if "clock level" in ln or "Mhz" in ln or "MHz" in ln]
+    return lines or None
 
 
 def bench_decode(steps: int = 256, replicas: int = 1):
@@ -213,26 +276,53 @@ def bench_copy(n_bytes: int = 1 << 30, reps: int = 5):
     return dict(bytes_each_way=n_bytes, ms=ms, GBps=2 * n_bytes / (ms * 1e-3) / 1e9)
 
 
-def cpu_baseline(calls: int = 3):
-    """The fp64 oracle on the first ``calls`` 32K-token calls of the same
-    long-context workload (state carried from call to call), heads spread over
-    the host's cores.  Input generation is not timed."""
-    from gated_delta_rule_amd import synth
+def cpu_baseline(host_calls):
+    """The fp64 oracle on the first three 32K calls of the same long-context
+    workload (state carried from call to call), heads spread over the host's
+    cores.  Input generation is not timed."""
     from oracle import gdr as ref
     procs = len(os.sched_getaffinity(0))
-    log(f"cpu baseline: fp64 oracle, {calls} x {T_CALL} tokens, 48 heads, {procs} processes")
+    log(f"cpu baseline: fp64 oracle, {len(host_calls)} x {T_CALL} tokens, 48 heads, {procs} processes")
     state, dt, used = None, 0.0, procs
-    for i in range(calls):
-        x = synth.long_context_call(i, T=T_CALL)
+    for x in host_calls:
         t0 = time.perf_counter()
         _, state, used = ref.forward_parallel(x.q, x.k, x.v, x.g, x.beta, state, processes=procs)
         dt += time.perf_counter() - t0
-        del x
-    tokens = calls * T_CALL
+    tokens = len(host_calls) * T_CALL
     return dict(value=tokens / dt, unit="tokens/s", cores=used, kind="oracle",
-                sample=f"fp64 token-serial oracle on the first {calls} 32768-token calls of the same "
+                sample=f"fp64 token-serial oracle on the first {len(host_calls)} 32768-token calls of the same "
                        f"16/48-head d=128 long-context workload, state carried between calls, heads spread "
                        f"over {used} processes: {tokens} tokens in {dt:.1f} s wall")
+
+
+def _decode_worker(args):
+    from oracle import gdr as ref
+    steps, lo, hi, s0 = args
+    s = s0
+    for xi in steps:
+        _, s = ref.decode_step(xi.q[lo:hi], xi.k[lo:hi], xi.v[lo:hi], xi.g[lo:hi], xi.beta[lo:hi], s)
+    return s
+
+
+def cpu_baseline_decode(steps: int = 4, N: int = 64):
+    """The fp64 oracle's decode step on the decode workload (64 sequences x 48
+    heads, 128x128 state), 4 steps, sequences spread over the host's cores."""
+    import multiprocessing as mp
+    from gated_delta_rule_amd import synth
+    procs = min(len(os.sched_getaffinity(0)), N)
+    _, _, s0 = synth.decode_inputs(N=N)
+    xs = [synth.decode_step_inputs(t, N=N) for t in range(steps)]
+    bounds = np.linspace(0, N, procs + 1).astype(int)
+    jobs = [(xs, int(a), int(b), s0[a:b]) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+    log(f"cpu baseline: fp64 oracle decode, {steps} steps of {N}x{HV} states, {len(jobs)} processes")
+    with mp.get_context("fork").Pool(len(jobs)) as pool:
+        t0 = time.perf_counter()
+        pool.map(_decode_worker, jobs)
+        dt = time.perf_counter() - t0
+    state_bytes = 2 * N * HV * D * D * 4 * steps
+    return dict(value=state_bytes / dt / 1e9, unit="GB/s (fp32 state bytes)", cores=len(jobs), kind="oracle",
+                sample=f"fp64 oracle decode step, {steps} steps of {N} sequences x {HV} heads (128x128 state), "
+                       f"sequences spread over {len(jobs)} processes: {dt:.2f} s wall")
 
 
 def traffic_from_counters():
@@ -248,11 +338,14 @@ def traffic_from_counters():
 
 
 def main():
+    global N_CALLS
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "pipeline", "copy"])
+    ap.add_argument("--steps", type=int, default=24)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "pipeline", "copy", "roofline"])
+    ap.add_argument("--pieces", type=int, default=N_CALLS,
+                    help="distinct 32K pieces of the context to cycle through (8 = the whole 262144 tokens)")
     ap.add_argument("--no-cpu", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -263,12 +356,21 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    N_CALLS = max(1, min(args.pieces, 8))
     out = {}
     if args.only == "copy":
         print(json.dumps({"copy": bench_copy()}), flush=True)
         return
+    if args.only == "roofline":
+        print(json.dumps({"achievable": bench_roofline()}), flush=True)
+        return
+    clocks_before = gpu_clocks()
+    host_calls = []
     if args.only in ("all", "prefill"):
-        pf = bench_prefill(args.steps, args.warmup)
+        log(f"prefill: generating {N_CALLS} x {T_CALL}-token pieces")
+        host_calls = long_context_host(N_CALLS)
+        pf = bench_prefill(args.steps, args.warmup, host_calls)
+        del host_calls[3:]
         ms_step = pf["total_ms"] / args.steps
         avg_launch_ms = float(np.mean(pf["recur_ms"]))
         bytes_launch = T_CALL * RECUR_BYTES_PER_TOKEN + 2 * STATE_BYTES
@@ -276,6 +378,7 @@ def main():
         call_bytes = T_CALL * PREFILL_BYTES_PER_TOKEN + 2 * STATE_BYTES
         traffic, tstat = traffic_from_counters()
         tok_s = T_CALL * args.steps / (pf["total_ms"] * 1e-3)
+        last_pass = pf["call_ms"][-N_CALLS:] if args.steps >= N_CALLS else None
         out.update({
             "metric": "prefill tokens/s per delta layer (T=32K) + decode state-update HBM GB/s",
             "value": tok_s,
@@ -289,8 +392,9 @@ def main():
             "vs_baseline": None,
             "dtype": "bf16",
             "data": "synthetic",
-            "config": {"workload": "delta-layer chunked prefill, 32768-token calls with state resume",
-                       "B": 1, "T_per_call": T_CALL, "num_k_heads": HK, "num_v_heads": HV, "head_dim": D,
+            "config": {"workload": f"delta-layer chunked prefill of a {N_CALLS * T_CALL}-token context as "
+                                   f"{N_CALLS} consecutive 32768-token calls with state resume",
+                       "B": 1, "T_per_call": T_CALL, "calls": N_CALLS, "num_k_heads": HK, "num_v_heads": HV, "head_dim": D,
                        "chunk": C, "qkv": "bf16", "gates_state_out": "fp32", "parallelism": "single GPU"},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
@@ -299,6 +403,8 @@ def main():
                          "mfma_frac": RECUR_FLOP_PER_TOKEN * T_CALL / (avg_launch_ms * 1e-3) / 1e12
                          / BF16_PEAK_TFLOPS},
             "call": {"prepare_ms": float(np.mean(pf["prep_ms"])), "recurrence_ms": avg_launch_ms,
+                     "median_ms": float(np.median(pf["call_ms"])),
+                     "context_ms": float(np.sum(last_pass)) if last_pass else None,
                      "hbm_frac": call_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "mfma_frac": PREFILL_FLOP_PER_TOKEN * T_CALL / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
             "finite": pf["finite"],
@@ -311,8 +417,20 @@ def main():
             out["decode_2_replicas"] = bench_decode(replicas=2)
     if args.only in ("all", "pipeline"):
         out["pipeline"] = bench_pipeline()
+    if args.only == "all":
+        ach = bench_roofline()
+        out["achievable"] = ach
+        if "roofline" in out:
+            out["roofline"]["frac_of_achievable"] = out["roofline"]["achieved"] / ach["hbm_rmw_nontemporal_GBps"]
+            out["roofline"]["mfma_frac_of_achievable"] = (out["roofline"]["mfma_frac"] * BF16_PEAK_TFLOPS
+                                                          / ach["mfma_bf16_TFLOPs"])
+        for key in ("decode", "decode_2_replicas"):
+            if key in out:
+                out[key]["frac_of_achievable"] = out[key]["state_GBps"] / ach["hbm_rmw_nontemporal_GBps"]
+    out["clocks"] = {"before": clocks_before, "after": gpu_clocks()}
     if args.only == "all" and not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline()
+        out["cpu_baseline"] = cpu_baseline(host_calls[:3] if host_calls else long_context_host(3))
+        out["cpu_baseline_decode"] = cpu_baseline_decode()
     print(json.dumps(out), flush=True)
 
 

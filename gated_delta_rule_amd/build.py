@@ -3,8 +3,9 @@
 Usage: python -m gated_delta_rule_amd.build [-v]
 
 Every source is compiled on each call (one hipcc process per file, in
-parallel) and linked into gated_delta_rule_amd/libgdr.so in place.
-Cross-compiles without a GPU.
+parallel) and linked into gated_delta_rule_amd/libgdr.so in place, next to
+libgdr_roofline.so (the roofline probes of include/gdr_roofline.h, which the
+benchmark uses).  Cross-compiles without a GPU.
 """
 from __future__ import annotations
 
@@ -19,6 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgdr.so")
+ROOFLINE_LIB = os.path.join(PKG, "libgdr_roofline.so")
 
 SOURCES = [
     "gdr_api.cpp",
@@ -28,6 +30,7 @@ SOURCES = [
     "kernels/conv_front.hip",
     "kernels/gated_rmsnorm.hip",
 ]
+ROOFLINE_SOURCES = ["roofline/roofline.hip"]
 
 ARCH = os.environ.get("GDR_OFFLOAD_ARCH", "gfx950")
 
@@ -64,19 +67,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libgdr.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"link of {os.path.basename(lib)} failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libgdr.so and libgdr_roofline.so; returns
+    the path of libgdr.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + ROOFLINE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], ROOFLINE_LIB, verbose)
     return LIB
 
 

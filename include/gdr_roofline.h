@@ -1,0 +1,52 @@
+/*
+ * Roofline probes for MI355X (gfx950): the achievable HBM bandwidth and bf16
+ * matrix-core rate of the machine they run on, measured beside the path's
+ * own kernels so that each kernel can be placed against what the hardware
+ * delivers as well as against the datasheet peaks (HBM 8 TB/s, dense bf16
+ * 2.5 PFLOP/s).  libgdr_roofline.so is a measurement aid and no part of the
+ * path's boundary (gdr.h).
+ *
+ * Each entry point only enqueues one kernel on `stream` (a hipStream_t, NULL
+ * for the default stream); the caller times it with events.  Buffers are
+ * caller-owned device memory, 16-byte aligned.  Return value: 0 on success,
+ * -1 for a bad argument (nothing launched), -3 if the launch failed.
+ */
+#ifndef GDR_ROOFLINE_H
+#define GDR_ROOFLINE_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * In-place read-modify-write stream: every 256-thread workgroup loads one
+ * 64 KiB slab (16 x 16 bytes per lane, all loads issued first), multiplies it
+ * by `scale` and stores it back -- the access pattern of the decode step.
+ * bytes: a positive multiple of 65536.  nontemporal != 0 streams past the
+ * last-level cache.  Traffic: 2 * bytes.
+ */
+int gdr_roofline_rmw(float* buf, size_t bytes, float scale, int nontemporal, void* stream);
+
+/*
+ * Read-only stream: every 256-thread workgroup sums one 64 KiB slab of `buf`
+ * and writes the sum to sums[workgroup] (bytes / 65536 floats).  bytes: a
+ * positive multiple of 65536.  Traffic: bytes (+ 4 bytes per 64 KiB).
+ */
+int gdr_roofline_read(const float* buf, size_t bytes, float* sums, void* stream);
+
+/*
+ * Dense bf16 matrix-core issue: `workgroups` workgroups of 256 threads, each
+ * wave running `iters` rounds of 8 independent v_mfma_f32_16x16x32_bf16 (16
+ * x 16 x 32 multiply-adds each); each wave writes one float of its
+ * accumulators to out[global wave index] (workgroups * 4 floats).
+ * FLOPs: workgroups * 4 * iters * 8 * 16384.  workgroups, iters > 0.
+ */
+int gdr_roofline_mfma(float* out, int workgroups, int iters, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_ROOFLINE_H */

@@ -1,0 +1,63 @@
+"""The roofline probe library: exports what include/gdr_roofline.h declares,
+rejects bad arguments before launching (CPU), and computes what it says (GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from gated_delta_rule_amd import roofline
+from helpers import gpu, say
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_match_header():
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "gdr_roofline.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(gdr_[a-z0-9_]+)\s*\(", text)))
+    assert declared == sorted(roofline.EXPORTED)
+    roofline.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", roofline.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(declared) <= exported
+
+
+def test_bad_arguments_rejected_before_launch():
+    lib = roofline.load()
+    fake = ctypes.c_void_p(1 << 20)
+    assert lib.gdr_roofline_rmw(None, 65536, 1.0, 0, None) == -1
+    assert lib.gdr_roofline_rmw(fake, 65536 + 16, 1.0, 0, None) == -1
+    assert lib.gdr_roofline_rmw(fake, 0, 1.0, 1, None) == -1
+    assert lib.gdr_roofline_read(fake, 65536, None, None) == -1
+    assert lib.gdr_roofline_read(fake, 1000, fake, None) == -1
+    assert lib.gdr_roofline_mfma(fake, 0, 10, None) == -1
+    assert lib.gdr_roofline_mfma(None, 4, 10, None) == -1
+
+
+@pytest.mark.gpu
+def test_probes_compute_what_they_say():
+    import torch
+    dev = gpu()
+    say("roofline probes: rmw, read, mfma")
+    n = 4 * 65536 // 4
+    x = torch.arange(n, device=dev, dtype=torch.float32) % 1000
+    ref = x.clone()
+    roofline.rmw(x, 2.0)
+    roofline.rmw(x, 0.5, nontemporal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(x, ref)
+    roofline.rmw(x, 3.0, nontemporal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(x, ref * 3.0)
+    sums = torch.empty(4, device=dev)
+    roofline.read(ref, sums)
+    torch.cuda.synchronize()
+    expect = ref.view(4, -1).double().sum(1).cpu().numpy()
+    assert np.allclose(sums.cpu().numpy(), expect, rtol=1e-6)
+    out = torch.full((8 * 4,), float("nan"), device=dev)
+    roofline.mfma(out, 8, 3)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
