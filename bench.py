@@ -23,7 +23,7 @@ in the same run:
   achievable -- the roofline probes (libgdr_roofline.so): streaming HBM
                read-modify-write and read rates and the dense bf16 matrix-core
                rate this GPU delivers, beside the datasheet peaks
-  clocks    -- rocm-smi's clock report before and after the run
+  clocks    -- the driver's current clock levels before and after the run
   cpu_baseline -- the fp64 CPU oracle timed on the host cores on a bounded
                sample of the same workload (the first three 32K-token calls;
                and 4 decode steps for the decode leg)
@@ -170,18 +170,21 @@ def bench_roofline(reps: int = 10):
 
 
 def gpu_clocks():
-    """rocm-smi's current clocks (text), or None if it cannot be read."""
-    import shutil
-    import subprocess
-    exe = shutil.which("rocm-smi") or ("/opt/rocm/bin/rocm-smi" if os.path.exists("/opt/rocm/bin/rocm-smi") else None)
-    if not exe:
-        return None
-    try:
-        r = subprocess.run([exe, "--showclocks"], capture_output=True, text=True, timeout=30)
-    except (OSError, subprocess.SubprocessError):
-        return None
-    lines = [ln.strip() for ln in r.stdout.splitlines() if "clock level" in ln or "Mhz" in ln or "MHz" in ln]
-    return lines or None
+    """Current shader and memory clock levels from the amdgpu driver's sysfs
+    files (the lines marked '*' of pp_dpm_sclk / pp_dpm_mclk), or None where
+    they cannot be read.  Read as files: no program is started."""
+    import glob
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                out[f"{os.path.basename(os.path.dirname(dev))}/{name}"] = cur[0]
+    return out or None
 
 
 def bench_decode(steps: int = 256, replicas: int = 1):
