@@ -187,16 +187,27 @@ def gpu_clocks():
     return out or None
 
 
-def bench_decode(steps: int = 256, replicas: int = 1):
+def bench_decode(steps: int = 256, replicas: int = 1, pool: int = 0):
+    """Decode steps of 64 sequences.  replicas > 1 cycles through that many
+    copies of the state set; pool > 0 keeps the states in a pool of that many
+    slots (gdr_recurrent_step_indexed) with the rows naming shuffled slots."""
     import torch
     import gated_delta_rule_amd as gdr
     from gated_delta_rule_amd import synth
     dev = torch.device("cuda:0")
     N = 64
-    log(f"decode: N={N}, {steps} steps, {replicas} state replica(s)")
+    log(f"decode: N={N}, {steps} steps, " + (f"pool of {pool} slots" if pool else f"{replicas} state replica(s)"))
     A_log, dt, s0 = synth.decode_inputs(N=N)
-    states = [torch.from_numpy(s0).to(dev) for _ in range(replicas)]
+    if pool:
+        perm = np.random.default_rng(7).permutation(pool)[:N]
+        slots = torch.zeros((pool, HV, D, D), device=dev)
+        slots[torch.as_tensor(perm, device=dev)] = torch.from_numpy(s0).to(dev)
+        idx = torch.as_tensor(perm.astype(np.int32), device=dev)
+        states = [slots]
+    else:
+        states = [torch.from_numpy(s0).to(dev) for _ in range(replicas)]
     del s0
+    kw = dict(state_indices=idx) if pool else {}
     inputs = []
     for s in range(steps):
         xi = synth.decode_step_inputs(s, N=N)
@@ -206,12 +217,12 @@ def bench_decode(steps: int = 256, replicas: int = 1):
                        torch.from_numpy(xi.g).to(dev), torch.from_numpy(xi.beta).to(dev)))
     o = torch.empty((N, HV, D), device=dev)
     for i in range(8):  # warmup
-        gdr.recurrent_step(*inputs[i], states[i % replicas], out=o)
+        gdr.recurrent_step(*inputs[i], states[i % len(states)], out=o, **kw)
     torch.cuda.synchronize()
     start, end = _events()
     start.record()
     for i in range(steps):
-        gdr.recurrent_step(*inputs[i], states[i % replicas], out=o)
+        gdr.recurrent_step(*inputs[i], states[i % len(states)], out=o, **kw)
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
@@ -418,6 +429,7 @@ def main():
         out["decode"] = bench_decode()
         if args.only == "all":
             out["decode_2_replicas"] = bench_decode(replicas=2)
+            out["decode_pool_indexed"] = bench_decode(pool=128)
     if args.only in ("all", "pipeline"):
         out["pipeline"] = bench_pipeline()
     if args.only == "all":
@@ -427,7 +439,7 @@ def main():
             out["roofline"]["frac_of_achievable"] = out["roofline"]["achieved"] / ach["hbm_rmw_nontemporal_GBps"]
             out["roofline"]["mfma_frac_of_achievable"] = (out["roofline"]["mfma_frac"] * BF16_PEAK_TFLOPS
                                                           / ach["mfma_bf16_TFLOPs"])
-        for key in ("decode", "decode_2_replicas"):
+        for key in ("decode", "decode_2_replicas", "decode_pool_indexed"):
             if key in out:
                 out[key]["frac_of_achievable"] = out[key]["state_GBps"] / ach["hbm_rmw_nontemporal_GBps"]
     out["clocks"] = {"before": clocks_before, "after": gpu_clocks()}

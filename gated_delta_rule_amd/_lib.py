@@ -23,6 +23,7 @@ EXPORTED = (
     "gdr_chunk_fwd_prepare",
     "gdr_chunk_fwd_recurrence",
     "gdr_recurrent_step",
+    "gdr_recurrent_step_indexed",
     "gdr_conv_gate_fused",
     "gdr_gated_rmsnorm",
 )
@@ -105,6 +106,8 @@ def load() -> ctypes.CDLL:
         fn.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]
     lib.gdr_recurrent_step.restype = I32
     lib.gdr_recurrent_step.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, P, P]
+    lib.gdr_recurrent_step_indexed.restype = I32
+    lib.gdr_recurrent_step_indexed.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, ctypes.c_int32, P, P, P]
     lib.gdr_conv_gate_fused.restype = I32
     lib.gdr_conv_gate_fused.argtypes = [ctypes.POINTER(GdrConvDesc)] + [P] * 15
     lib.gdr_gated_rmsnorm.restype = I32

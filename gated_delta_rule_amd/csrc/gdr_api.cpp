@@ -196,12 +196,15 @@ gdr_status gdr_chunk_fwd_recurrence(const gdr_desc* d, const void* q, const void
                    stream, gdr::kStageRecur, "gdr_chunk_fwd_recurrence launch");
 }
 
-gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
-                              const float* beta, float* state, void* o, void* stream) {
+static gdr_status recurrent_step(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, float* state, int32_t pool_size, const int32_t* state_indices,
+                                 void* o, void* stream, const char* name) {
   gdr_status st = check_desc(d, true, false);
   if (st != GDR_OK) return st;
   if (d->batch == 0) return ok();
-  if (!q || !k || !v || !g || !beta || !state || !o)
+  // an empty pool (every row padding) may be NULL
+  const bool empty_pool = state_indices && pool_size == 0;
+  if (!q || !k || !v || !g || !beta || (!state && !empty_pool) || !o)
     return fail(GDR_ERR_INVALID_ARG, "q, k, v, g, beta, state and o are required");
   if (!aligned16(state)) return fail(GDR_ERR_INVALID_ARG, "state must be 16-byte aligned");
   gdr::DecodeArgs a{};
@@ -211,6 +214,8 @@ gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, c
   a.g = g;
   a.beta = beta;
   a.state = state;
+  a.state_indices = state_indices;
+  a.pool_size = pool_size;
   a.o = o;
   a.N = d->batch;
   a.Hk = d->num_k_heads;
@@ -221,7 +226,21 @@ gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, c
   a.use_l2 = d->use_qk_l2norm != 0;
   a.scale = d->scale;
   a.eps = d->l2norm_eps;
-  return hip_status(gdr::launch_decode(a, static_cast<hipStream_t>(stream)), "gdr_recurrent_step launch");
+  return hip_status(gdr::launch_decode(a, static_cast<hipStream_t>(stream)), name);
+}
+
+gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                              const float* beta, float* state, void* o, void* stream) {
+  return recurrent_step(d, q, k, v, g, beta, state, 0, nullptr, o, stream, "gdr_recurrent_step launch");
+}
+
+gdr_status gdr_recurrent_step_indexed(const gdr_desc* d, const void* q, const void* k, const void* v,
+                                      const float* g, const float* beta, float* state_pool, int32_t pool_size,
+                                      const int32_t* state_indices, void* o, void* stream) {
+  if (pool_size < 0) return fail(GDR_ERR_INVALID_ARG, "pool_size must be >= 0 (got %d)", pool_size);
+  if (!state_indices) return fail(GDR_ERR_INVALID_ARG, "state_indices is required");
+  return recurrent_step(d, q, k, v, g, beta, state_pool, pool_size, state_indices, o, stream,
+                        "gdr_recurrent_step_indexed launch");
 }
 
 gdr_status gdr_conv_gate_fused(const gdr_conv_desc* d, const void* x, const void* conv_w,

@@ -13,6 +13,8 @@ struct DecodeArgs {
   const void *q, *k, *v;
   const float *g, *beta;
   float* state;
+  const int32_t* state_indices;  // NULL: sequence n uses state n; else a pool slot
+  int pool_size;                 // slots of the pool (with state_indices)
   void* o;
   int N, Hk, Hv, D;
   int qkv_bf16, out_bf16, use_l2;

@@ -54,6 +54,7 @@ template <int D, typename TQ, typename TO>
 __global__ __launch_bounds__(256) void decode_kernel(const TQ* __restrict__ q, const TQ* __restrict__ k,
                                                      const TQ* __restrict__ v, const float* __restrict__ g,
                                                      const float* __restrict__ beta, float* __restrict__ state,
+                                                     const int32_t* __restrict__ state_indices, int pool_size,
                                                      TO* __restrict__ o, int Hk, int Hv, int use_l2,
                                                      float scale, float eps) {
   constexpr int F4 = D / 32;                 // 16-byte pieces per lane per row
@@ -65,8 +66,19 @@ __global__ __launch_bounds__(256) void decode_kernel(const TQ* __restrict__ q, c
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane >> 3, e8 = lane & 7;
 
-  float* S = state + (size_t)nh * D * D;
   const int row0 = part * (D / SPLIT) + wave * (D / (4 * SPLIT)) + sub;
+  // State slot of sequence n: n itself, or its pool index.  A padding row
+  // (index outside [0, pool_size)) writes zeros for its outputs and touches
+  // no state.
+  const int slot = state_indices ? state_indices[n] : n;
+  if (state_indices && (slot < 0 || slot >= pool_size)) {
+    TO* op = o + (size_t)nh * D;
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+      if (e8 == 0) store_from_f32(op + row0 + 8 * i, 0.f);
+    return;
+  }
+  float* S = state + ((size_t)slot * Hv + h) * D * D;
 
   // Issue every state load first: NS * F4 x 16 B per lane in flight.
   f32x4 s[NS][F4];
@@ -146,7 +158,8 @@ template <int D, typename TQ, typename TO>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_kernel<D, TQ, TO>), dim3(a.N * a.Hv * kDecodeSplit<D>), dim3(256), 0, st,
                      static_cast<const TQ*>(a.q), static_cast<const TQ*>(a.k), static_cast<const TQ*>(a.v),
-                     a.g, a.beta, a.state, static_cast<TO*>(a.o), a.Hk, a.Hv, a.use_l2, a.scale, a.eps);
+                     a.g, a.beta, a.state, a.state_indices, a.pool_size, static_cast<TO*>(a.o), a.Hk, a.Hv,
+                     a.use_l2, a.scale, a.eps);
   return hipGetLastError();
 }
 

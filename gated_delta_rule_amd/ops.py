@@ -139,10 +139,15 @@ def chunk_workspace(q: torch.Tensor, v: torch.Tensor, cu_seqlens: Optional[torch
 
 def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
                    state: torch.Tensor, use_qk_l2norm_in_kernel: bool = True, scale: float = 1.0,
-                   out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """One decode token (gdr_recurrent_step); ``state`` [N, Hv, d, d] is updated in place.
+                   out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+                   state_indices: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode token (gdr_recurrent_step); the states are updated in place.
 
     q, k: [N, Hk, d]; v: [N, Hv, d]; g, beta: [N, Hv] fp32.  Returns o [N, Hv, d].
+    Without ``state_indices``, ``state`` is [N, Hv, d, d].  With it (int32 [N],
+    gdr_recurrent_step_indexed), ``state`` is a pool [P, Hv, d, d] and sequence
+    n updates slot state_indices[n]; an index outside [0, P) marks a padding
+    row (o = 0, no slot touched).
     """
     dev = q.device
     qd = q.dtype
@@ -155,17 +160,30 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     _need(state, "state", (torch.float32,), dev)
     N, Hk, D = q.shape
     Hv = v.shape[1]
-    if k.shape != q.shape or v.shape != (N, Hv, D) or g.shape != (N, Hv) or beta.shape != (N, Hv) \
-            or state.shape != (N, Hv, D, D):
-        raise ValueError("shape mismatch among q, k, v, g, beta, state")
+    if k.shape != q.shape or v.shape != (N, Hv, D) or g.shape != (N, Hv) or beta.shape != (N, Hv):
+        raise ValueError("shape mismatch among q, k, v, g, beta")
+    if state_indices is None:
+        if state.shape != (N, Hv, D, D):
+            raise ValueError(f"state must be {(N, Hv, D, D)}")
+    else:
+        _need(state_indices, "state_indices", (torch.int32,), dev)
+        if state_indices.shape != (N,) or state.dim() != 4 or state.shape[1:] != (Hv, D, D):
+            raise ValueError(f"state_indices must be [{N}] and state a pool [P, {Hv}, {D}, {D}]")
     if out is None:
         out = torch.empty((N, Hv, D), device=dev, dtype=out_dtype)
     else:
         _need(out, "out", (out_dtype,), dev)
     desc = make_desc(N, 1, N, Hk, Hv, D, 64, qd, out_dtype, use_qk_l2norm_in_kernel, scale, 1e-6)
-    st = _lib.load().gdr_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                        _ptr(state), _ptr(out), _stream(dev))
-    _lib.check("gdr_recurrent_step", st)
+    lib = _lib.load()
+    if state_indices is None:
+        st = lib.gdr_recurrent_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(state), _ptr(out), _stream(dev))
+        _lib.check("gdr_recurrent_step", st)
+    else:
+        st = lib.gdr_recurrent_step_indexed(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                            _ptr(state) if state.numel() else None, state.shape[0],
+                                            _ptr(state_indices), _ptr(out), _stream(dev))
+        _lib.check("gdr_recurrent_step_indexed", st)
     return out
 
 

@@ -181,6 +181,30 @@ gdr_status gdr_recurrent_step(const gdr_desc* d, const void* q, const void* k, c
                               void* stream);
 
 /*
+ * gdr_recurrent_step on states kept in a persistent pool, as a serving
+ * cache does (yfxerp page, section 1.2: the delta-rule layers keep their
+ * recurrent state in a cache layer of their own, apart from the attention
+ * layers' key/value cache).  Sequence n updates pool slot state_indices[n].
+ *
+ *   state_pool    [pool_size, Hv, d_v, d_k] fp32, slots read and overwritten
+ *                 IN PLACE
+ *   state_indices [N] int32 device array; an entry < 0 or >= pool_size marks
+ *                 a padding row: its o is written as zeros and no slot is
+ *                 read or written.  The other entries must be distinct (two
+ *                 rows updating one slot would race).
+ *   everything else as gdr_recurrent_step.
+ *
+ * Errors: as gdr_recurrent_step; INVALID_ARG also for pool_size < 0 or a NULL
+ * state_indices.  state_pool may be NULL only when pool_size is 0 (every row
+ * padding).  With state_indices[n] = n and pool_size = N the result is
+ * bit-identical to gdr_recurrent_step.
+ */
+gdr_status gdr_recurrent_step_indexed(const gdr_desc* d, const void* q, const void* k, const void* v,
+                                      const float* g, const float* beta, float* state_pool,
+                                      int32_t pool_size, const int32_t* state_indices, void* o,
+                                      void* stream);
+
+/*
  * Front of the layer: depthwise causal conv (kernel 4, no bias) + SiLU over
  * all C = 2*Hk*d + Hv*d channels, plus the gates (deepmagic page: kernel-4
  * causal conv in front; yfxerp page, section 1.2: beta = sigmoid(b),

@@ -50,6 +50,7 @@ __all__ = [
     "forward",
     "forward_parallel",
     "decode_step",
+    "decode_step_pool",
     "chunked",
 ]
 
@@ -200,6 +201,35 @@ def decode_step(q, k, v, g, beta, state, *, use_qk_l2norm: bool = True,
     o, S = recurrence(S0, np.exp(flat(g)), flat(beta), flat(k[:, kmap]), flat(v),
                       flat(q[:, kmap]), scale)
     return o.reshape(N, hv, dv), S.reshape(N, hv, dv, dk)
+
+
+def decode_step_pool(q, k, v, g, beta, pool, state_indices, *, use_qk_l2norm: bool = True,
+                     eps: float = 1e-6, scale: float = 1.0):
+    """decode_step on states kept in a pool (yfxerp page, section 1.2: the
+    delta-rule layers keep their recurrent state in a cache layer of their
+    own).  Row n updates pool[state_indices[n]]; an index outside
+    [0, len(pool)) marks a padding row, whose o is zero and which touches no
+    slot.  Valid indices must be distinct.
+
+    Returns (o [N, Hv, dv], new_pool), both float64; slots no row names keep
+    their values.
+    """
+    idx = np.asarray(state_indices, dtype=np.int64)
+    pool = np.asarray(pool, dtype=np.float64)
+    live = (idx >= 0) & (idx < len(pool))
+    if len(np.unique(idx[live])) != int(live.sum()):
+        raise ValueError("state_indices name a slot twice")
+    N, hv, dv = len(idx), np.shape(v)[1], np.shape(v)[2]
+    o = np.zeros((N, hv, dv))
+    new_pool = pool.copy()
+    if live.any():
+        rows = np.flatnonzero(live)
+        sel = lambda x: np.asarray(x)[rows]
+        o_live, s_live = decode_step(sel(q), sel(k), sel(v), sel(g), sel(beta), pool[idx[rows]],
+                                     use_qk_l2norm=use_qk_l2norm, eps=eps, scale=scale)
+        o[rows] = o_live
+        new_pool[idx[rows]] = s_live
+    return o, new_pool
 
 
 def chunked(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, chunk_size: int = 64,

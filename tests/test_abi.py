@@ -121,6 +121,12 @@ def test_recurrent_step_validation():
     assert lib.gdr_recurrent_step(ctypes.byref(d), *args, None, FAKE, None) == -1
     assert lib.gdr_recurrent_step(ctypes.byref(d), *args, FAKE + 8, FAKE, None) == -1
     assert "aligned" in lib.gdr_last_error().decode()
+    ix = lib.gdr_recurrent_step_indexed
+    assert ix(ctypes.byref(d), *args, FAKE, -1, FAKE, FAKE, None) == -1 and "pool_size" in lib.gdr_last_error().decode()
+    assert ix(ctypes.byref(d), *args, FAKE, 8, None, FAKE, None) == -1 and "state_indices" in lib.gdr_last_error().decode()
+    assert ix(ctypes.byref(d), *args, None, 8, FAKE, FAKE, None) == -1  # a NULL pool only when it is empty
+    assert ix(ctypes.byref(d), *args, FAKE + 8, 8, FAKE, FAKE, None) == -1
+    assert ix(ctypes.byref(_desc(batch=4, num_seqs=4, seq_len=2)), *args, FAKE, 8, FAKE, FAKE, None) == -1
 
 
 def test_conv_and_norm_validation():

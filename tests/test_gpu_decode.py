@@ -133,3 +133,56 @@ def test_decode_reset_and_no_write():
     o_ref, s_ref = ref.decode_step(x.q, x.k, x.v, g, beta, s0.astype(np.float64))
     assert rel_err(to_host(o), o_ref) <= BF16_TOL and rel_err(to_host(state), s_ref) <= BF16_TOL
     assert np.array_equal(to_host(state)[1], s0[1])
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("f32", 32)])
+def test_decode_pool_indexed(dtype, d):
+    """gdr_recurrent_step_indexed on a pool of 40 slots: 16 rows naming distinct
+    slots in shuffled order, plus padding rows (index -1 and >= pool size) over
+    3 steps; o and the whole pool against the oracle, unnamed slots bit for bit."""
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    N, P, hk, hv = 20, 40, (16 if d == 128 else 2), (48 if d == 128 else 6)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    rng = np.random.default_rng(70 + d)
+    idx = np.concatenate([rng.choice(P, 16, replace=False), [-1, P, P + 7, -5]]).astype(np.int32)
+    rng.shuffle(idx)
+    pool0 = (0.05 * rng.standard_normal((P, hv, d, d))).astype(np.float32)
+    pool = to_dev(pool0, "f32", dev)
+    ref_pool = pool0.astype(np.float64)
+    di = torch.as_tensor(idx, device=dev)
+    say(f"decode pool-indexed {dtype} d={d}: {N} rows, pool {P}")
+    for step in range(3):
+        x = synth.decode_step_inputs(step, N=N, hk=hk, hv=hv, d=d, dtype=dtype)
+        o = gdr_amd.recurrent_step(to_dev(x.q, dtype, dev), to_dev(x.k, dtype, dev), to_dev(x.v, dtype, dev),
+                                   to_dev(x.g, "f32", dev), to_dev(x.beta, "f32", dev), pool, state_indices=di)
+        o_ref, ref_pool = ref.decode_step_pool(x.q, x.k, x.v, x.g, x.beta, ref_pool, idx)
+        og = to_host(o)
+        pad = (idx < 0) | (idx >= P)
+        assert np.all(og[pad] == 0)
+        assert rel_err(og[~pad], o_ref[~pad]) <= tol
+    torch.cuda.synchronize()
+    gp = to_host(pool)
+    live = sorted(int(i) for i in idx if 0 <= i < P)
+    dead = [p for p in range(P) if p not in set(live)]
+    assert np.array_equal(gp[dead], pool0[dead])
+    assert rel_err(gp[live], ref_pool[live]) <= tol
+
+
+def test_decode_pool_identity_equals_plain_bit_exact():
+    """Indices 0..N-1 over a pool of N slots give the plain call's bits."""
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    N = 8
+    A_log, dt, s0 = synth.decode_inputs(N=N)
+    x = synth.decode_step_inputs(0, N=N)
+    args = [to_dev(a, t, dev) for a, t in ((x.q, "bf16"), (x.k, "bf16"), (x.v, "bf16"), (x.g, "f32"),
+                                          (x.beta, "f32"))]
+    s1, s2 = to_dev(s0, "f32", dev), to_dev(s0, "f32", dev)
+    say("decode pool identity vs plain")
+    o1 = gdr_amd.recurrent_step(*args, s1)
+    o2 = gdr_amd.recurrent_step(*args, s2, state_indices=torch.arange(N, device=dev, dtype=torch.int32))
+    torch.cuda.synchronize()
+    assert bits_equal(o1, o2) and bits_equal(s1, s2)

@@ -316,6 +316,32 @@ def test_decode_step_equals_one_token_prefill():
     np.testing.assert_allclose(S, S_ref, rtol=1e-14, atol=1e-15)
 
 
+def test_decode_step_pool_indexing():
+    """Pool decode = per-row one-token prefill from the named slot; padding rows
+    (index < 0 or >= pool size) give o = 0; unnamed slots keep their values."""
+    r = np.random.default_rng(28)
+    N, hk, hv, d, P = 6, 2, 6, 8, 9
+    q, k = r.standard_normal((2, N, hk, d))
+    v = r.standard_normal((N, hv, d))
+    g = -np.abs(r.standard_normal((N, hv)))
+    beta = r.uniform(0, 1, (N, hv))
+    pool = r.standard_normal((P, hv, d, d))
+    idx = np.array([7, -1, 0, 4, 9, 2])
+    o, new = gdr.decode_step_pool(q, k, v, g, beta, pool, idx)
+    for n in range(N):
+        if 0 <= idx[n] < P:
+            o1, s1 = gdr.forward(q[n:n + 1, None], k[n:n + 1, None], v[n:n + 1, None], g[n:n + 1, None],
+                                 beta[n:n + 1, None], pool[idx[n]][None])
+            np.testing.assert_allclose(o[n], o1[0, 0], rtol=1e-14, atol=1e-15)
+            np.testing.assert_allclose(new[idx[n]], s1[0], rtol=1e-14, atol=1e-15)
+        else:
+            assert np.all(o[n] == 0)
+    untouched = [p for p in range(P) if p not in set(idx.tolist())]
+    assert np.array_equal(new[untouched], pool[untouched])
+    with pytest.raises(ValueError):
+        gdr.decode_step_pool(q, k, v, g, beta, pool, np.array([1, 1, -1, 2, 3, 4]))
+
+
 def test_parallel_equals_serial():
     q, k, v, g, beta = _rand_inputs(27, T=20, hk=2, hv=6)
     o, S = gdr.forward(q, k, v, g, beta)
