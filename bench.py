@@ -233,6 +233,69 @@ def bench_decode(steps: int = 256, replicas: int = 1, pool: int = 0):
                 frac_hbm=state_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, working_set_MiB=replicas * state_bytes / 2 / 2**20)
 
 
+def bench_decode_layer(steps: int = 128):
+    """One decode token of the whole layer path for 64 sequences: the fused
+    gdr_decode_layer_step against the same work as three launches
+    (gdr_conv_gate_fused on one-token sequences, gdr_recurrent_step,
+    gdr_gated_rmsnorm).  Bytes counted: the recurrent state read and written,
+    plus x, the conv state (read and written), a, b, z and y."""
+    import torch
+    import gated_delta_rule_amd as gdr
+    from gated_delta_rule_amd import synth
+    dev = torch.device("cuda:0")
+    N = 64
+    C = (2 * HK + HV) * D
+    log(f"decode layer: N={N}, {steps} steps, fused vs three launches")
+    p0 = synth.pipeline_inputs(seed=7, lengths=[1] * N)
+    A_log, dt, s0 = synth.decode_inputs(N=N)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).to(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    cw, nw, Al, dtb = bf(p0.conv_w), f32(p0.norm_w), f32(A_log), f32(dt)
+    rng = np.random.default_rng(8)
+    conv_state = bf(synth.round_bf16(rng.standard_normal((N, C, 3))))
+    state = f32(s0)
+    del s0
+    steps_in = []
+    for s in range(steps):
+        pi = synth.pipeline_inputs(seed=200 + s, lengths=[1] * N)
+        steps_in.append((bf(pi.x), f32(pi.a), f32(pi.b), bf(pi.z)))
+    cu = torch.arange(N + 1, device=dev, dtype=torch.int32)
+
+    def fused(i):
+        x, a, b, z = steps_in[i % steps]
+        gdr.decode_layer_step(x, cw, conv_state, a, b, Al, dtb, state, z, nw, HK, HV)
+
+    cs_out = torch.empty_like(conv_state)
+
+    def unfused(i):
+        x, a, b, z = steps_in[i % steps]
+        q, k, v, g, beta, _ = gdr.conv_gate_fused(x, cw, cu, a, b, Al, dtb, HK, HV, D, conv_state_in=conv_state,
+                                                  output_conv_state=False)
+        o = gdr.recurrent_step(q[0], k[0], v[0], g[0], beta[0], state)
+        gdr.gated_rmsnorm(o.reshape(1, N, HV, D), z.reshape(1, N, HV * D), nw)
+
+    def timed(fn):
+        for i in range(8):
+            fn(i)
+        torch.cuda.synchronize()
+        start, end = _events()
+        start.record()
+        for i in range(steps):
+            fn(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    ms_f = timed(fused)
+    ms_u = timed(unfused)
+    state_bytes = 2 * N * HV * D * D * 4
+    other = N * (C * 2 + 2 * C * 3 * 2 + 2 * HV * 4 + 2 * HV * D * 2)
+    return dict(us_per_step=ms_f * 1e3, state_GBps=state_bytes / (ms_f * 1e-3) / 1e9,
+                total_GBps=(state_bytes + other) / (ms_f * 1e-3) / 1e9,
+                frac_hbm=state_bytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                three_launches_us_per_step=ms_u * 1e3)
+
+
 def bench_pipeline(reps: int = 5):
     import torch
     import gated_delta_rule_amd as gdr
@@ -430,6 +493,7 @@ def main():
         if args.only == "all":
             out["decode_2_replicas"] = bench_decode(replicas=2)
             out["decode_pool_indexed"] = bench_decode(pool=128)
+            out["decode_layer"] = bench_decode_layer()
     if args.only in ("all", "pipeline"):
         out["pipeline"] = bench_pipeline()
     if args.only == "all":
@@ -439,7 +503,7 @@ def main():
             out["roofline"]["frac_of_achievable"] = out["roofline"]["achieved"] / ach["hbm_rmw_nontemporal_GBps"]
             out["roofline"]["mfma_frac_of_achievable"] = (out["roofline"]["mfma_frac"] * BF16_PEAK_TFLOPS
                                                           / ach["mfma_bf16_TFLOPs"])
-        for key in ("decode", "decode_2_replicas", "decode_pool_indexed"):
+        for key in ("decode", "decode_2_replicas", "decode_pool_indexed", "decode_layer"):
             if key in out:
                 out[key]["frac_of_achievable"] = out[key]["state_GBps"] / ach["hbm_rmw_nontemporal_GBps"]
     out["clocks"] = {"before": clocks_before, "after": gpu_clocks()}

@@ -9,6 +9,7 @@ from .ops import (  # noqa: F401
     chunk_gated_delta_rule,
     chunk_workspace,
     conv_gate_fused,
+    decode_layer_step,
     gated_rmsnorm,
     recurrent_step,
 )
@@ -19,6 +20,7 @@ __all__ = [
     "chunk_gated_delta_rule",
     "chunk_workspace",
     "recurrent_step",
+    "decode_layer_step",
     "conv_gate_fused",
     "gated_rmsnorm",
 ]

@@ -24,6 +24,7 @@ EXPORTED = (
     "gdr_chunk_fwd_recurrence",
     "gdr_recurrent_step",
     "gdr_recurrent_step_indexed",
+    "gdr_decode_layer_step",
     "gdr_conv_gate_fused",
     "gdr_gated_rmsnorm",
 )
@@ -108,6 +109,9 @@ def load() -> ctypes.CDLL:
     lib.gdr_recurrent_step.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, P, P]
     lib.gdr_recurrent_step_indexed.restype = I32
     lib.gdr_recurrent_step_indexed.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, ctypes.c_int32, P, P, P]
+    lib.gdr_decode_layer_step.restype = I32
+    lib.gdr_decode_layer_step.argtypes = ([ctypes.POINTER(GdrDesc)] + [P] * 8 + [ctypes.c_int32, P, P, P, F]
+                                          + [P] * 4)
     lib.gdr_conv_gate_fused.restype = I32
     lib.gdr_conv_gate_fused.argtypes = [ctypes.POINTER(GdrConvDesc)] + [P] * 15
     lib.gdr_gated_rmsnorm.restype = I32

@@ -25,6 +25,7 @@ ROOFLINE_LIB = os.path.join(PKG, "libgdr_roofline.so")
 SOURCES = [
     "gdr_api.cpp",
     "kernels/decode.hip",
+    "kernels/decode_layer.hip",
     "kernels/chunk_f32.hip",
     "kernels/chunk_bf16.hip",
     "kernels/conv_front.hip",

@@ -79,4 +79,19 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+
+// Sum over the 8-lane group (lanes 8m .. 8m+7) with data-parallel-primitive
+// moves (no LDS traffic); every lane gets the same value, since each step
+// adds a lane pair in both orders.
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  x += dpp_move<0x141>(x);  // row_half_mirror: lane i <-> 7 - i of its 8
+  return x;
+}
+
 }  // namespace gdr

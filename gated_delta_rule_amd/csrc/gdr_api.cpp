@@ -243,6 +243,53 @@ gdr_status gdr_recurrent_step_indexed(const gdr_desc* d, const void* q, const vo
                         "gdr_recurrent_step_indexed launch");
 }
 
+gdr_status gdr_decode_layer_step(const gdr_desc* d, const void* x, const void* conv_w, void* conv_state,
+                                 const float* a, const float* b, const float* A_log, const float* dt_bias,
+                                 float* state, int32_t pool_size, const int32_t* state_indices, const void* z,
+                                 const float* norm_w, float norm_eps, void* y, float* o, void* qkv_out,
+                                 void* stream) {
+  gdr_status st = check_desc(d, true, false);
+  if (st != GDR_OK) return st;
+  if (d->head_dim_k != 128 || d->head_dim_v != 128)
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_decode_layer_step supports d = 128 (got %d)", d->head_dim_k);
+  const int G = d->num_v_heads / d->num_k_heads;
+  if (G < 1 || G > 4)
+    return fail(GDR_ERR_UNSUPPORTED, "gdr_decode_layer_step supports Hv/Hk in 1..4 (got %d)", G);
+  if (d->qkv_dtype != GDR_BF16) return fail(GDR_ERR_UNSUPPORTED, "gdr_decode_layer_step takes bf16 x");
+  if (pool_size < 0) return fail(GDR_ERR_INVALID_ARG, "pool_size must be >= 0 (got %d)", pool_size);
+  if (d->batch == 0) return ok();
+  const bool empty_pool = state_indices && pool_size == 0;
+  if (!x || !conv_w || !a || !b || !A_log || !dt_bias || !z || !norm_w || !y ||
+      ((!state || !conv_state) && !empty_pool))
+    return fail(GDR_ERR_INVALID_ARG, "x, conv_w, conv_state, a, b, A_log, dt_bias, state, z, norm_w and y are required");
+  if (!aligned16(state) || reinterpret_cast<uintptr_t>(conv_w) % 8)
+    return fail(GDR_ERR_INVALID_ARG, "state must be 16-byte and conv_w 8-byte aligned");
+  gdr::LayerStepArgs la{};
+  la.x = x;
+  la.conv_w = conv_w;
+  la.conv_state = conv_state;
+  la.a = a;
+  la.b = b;
+  la.A_log = A_log;
+  la.dt_bias = dt_bias;
+  la.state = state;
+  la.state_indices = state_indices;
+  la.pool_size = pool_size;
+  la.z = z;
+  la.norm_w = norm_w;
+  la.y = y;
+  la.o = o;
+  la.qkv_out = qkv_out;
+  la.N = d->batch;
+  la.Hk = d->num_k_heads;
+  la.Hv = d->num_v_heads;
+  la.use_l2 = d->use_qk_l2norm != 0;
+  la.scale = d->scale;
+  la.eps = d->l2norm_eps;
+  la.norm_eps = norm_eps;
+  return hip_status(gdr::launch_decode_layer(la, static_cast<hipStream_t>(stream)), "gdr_decode_layer_step launch");
+}
+
 gdr_status gdr_conv_gate_fused(const gdr_conv_desc* d, const void* x, const void* conv_w,
                                const int32_t* cu_seqlens, const void* conv_state_in, void* conv_state_out,
                                const float* a, const float* b, const float* A_log, const float* dt_bias,

@@ -44,6 +44,24 @@ struct ConvArgs {
   int T, N, Hk, Hv, D;
 };
 
+struct LayerStepArgs {
+  const void* x;           // [N, C] bf16 token projections (q | k | v)
+  const void* conv_w;      // [C, 4] bf16
+  void* conv_state;        // [P, C, 3] bf16, rolled in place
+  const float *a, *b;      // [N, Hv]
+  const float *A_log, *dt_bias;  // [Hv]
+  float* state;            // [P, Hv, d, d] fp32, in place
+  const int32_t* state_indices;  // NULL: row n uses slot n
+  int pool_size;
+  const void* z;           // [N, Hv*d] bf16
+  const float* norm_w;     // [d]
+  void* y;                 // [N, Hv*d] bf16
+  float* o;                // [N, Hv, d] fp32 or NULL
+  void* qkv_out;           // [N, C] bf16 or NULL
+  int N, Hk, Hv, use_l2;
+  float scale, eps, norm_eps;
+};
+
 struct NormArgs {
   const void* o;
   const void* z;
@@ -54,6 +72,7 @@ struct NormArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_layer(const LayerStepArgs& a, hipStream_t st);
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t st);
 // The bf16-MFMA prefill needs a device workspace of
 // chunk_bf16_workspace_bytes(a) bytes (chunk table + per-chunk records).  It

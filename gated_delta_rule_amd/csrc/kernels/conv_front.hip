@@ -22,6 +22,7 @@
 // once; a run of 8 keeps the fully unrolled body in the instruction cache.
 #include "../common.h"
 #include "../internal.h"
+#include "../silu32.h"
 
 #pragma clang fp contract(off)
 
@@ -31,47 +32,6 @@ namespace {
 
 constexpr int kConvThreads = 256;
 constexpr int kConvRun = 8;  // tokens per thread
-
-// Cody-Waite reduction and the Taylor polynomial scaled by 2^n, with no
-// special cases (exp32 for x in [kExpLo, kExpHi]).
-__device__ __forceinline__ float exp_poly(float x) {
-  const float n = __builtin_rintf(x * 0x1.715476p+0f);
-  const float r = (x - n * 0x1.630000p-1f) - n * -0x1.bd0106p-13f;
-  float p = 0x1.a01a02p-13f;
-  p = p * r + 0x1.6c16c2p-10f;
-  p = p * r + 0x1.111112p-7f;
-  p = p * r + 0x1.555556p-5f;
-  p = p * r + 0x1.555556p-3f;
-  p = p * r + 0x1.0p-1f;
-  p = p * r + 1.0f;
-  p = p * r + 1.0f;
-  return __builtin_ldexpf(p, static_cast<int>(n));
-}
-
-// exp32 is +inf above kExpHi = 0x1.62e430p+6 (about 88.72) and 0 below kExpLo.
-constexpr float kExpLo = -0x1.9fe368p+6f;
-
-// SiLU by the contract for every v.  exp32(-v) is taken as exp_poly on -v
-// clamped into [kExpLo, 128], which gives the same quotient: above kExpHi the
-// scale by 2^n overflows to +inf for every x up to 128, as exp32 does; below
-// kExpLo the clamped value is at most 2^-149, so 1 + e rounds to 1, as it does
-// for exp32's 0; a NaN v stays NaN through the division.
-__device__ __forceinline__ float silu32(float v) {
-  return v / (1.0f + exp_poly(fminf(fmaxf(-v, kExpLo), 128.f)));
-}
-
-// SiLU for |v| <= 80, where no clamp is needed and the IEEE division can be
-// replaced by one residual correction of v * rcp(d): q0 = v y0, r = d q0 - v
-// (exact by the fused multiply-add), q = q0 - r y0.  The residual is taken
-// as d q0 - v rather than v - d q0 so that v = -0 keeps its sign.  Checked
-// equal, bit for bit, to silu32 for every fp32 v in [-80, 80].
-__device__ __forceinline__ float silu32_mid(float v) {
-  const float d = 1.0f + exp_poly(-v);
-  const float y0 = __builtin_amdgcn_rcpf(d);
-  const float q0 = v * y0;
-  const float rn = __builtin_fmaf(d, q0, -v);
-  return __builtin_fmaf(-rn, y0, q0);
-}
 
 // Sequence index n with cu[n] <= t < cu[n+1] (empty sequences skipped).
 __device__ __forceinline__ int seq_of(const int32_t* cu, int N, int t) {
@@ -194,10 +154,7 @@ __global__ __launch_bounds__(kConvThreads) void conv_front_kernel(ConvArgs a) {
     const int t = t0 + e / a.Hv, hh = e % a.Hv;
     if (t < a.T) {
       const size_t i = (size_t)t * a.Hv + hh;
-      const float x = a.a[i] + a.dt_bias[hh];
-      const float sp = fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
-      a.g[i] = -expf(a.A_log[hh]) * sp;
-      a.beta[i] = 1.f / (1.f + expf(-a.b[i]));
+      gates(a.a[i], a.b[i], a.A_log[hh], a.dt_bias[hh], a.g[i], a.beta[i]);
     }
   }
 }

@@ -29,24 +29,11 @@ namespace gdr {
 
 namespace {
 
-// Sum over the 8-lane group (lanes 8m .. 8m+7); every lane gets the same
-// value (each step adds a lane pair in both orders).
 // Workgroups per state: at d = 128 two, each streaming 64 of the 128 rows,
 // so that a lane holds 32 state registers and more workgroups share a
 // compute unit (every state row is independent given k, q, v and the gates).
 template <int D>
 constexpr int kDecodeSplit = D == 128 ? 2 : 1;
-
-template <int kCtrl>
-__device__ __forceinline__ float dpp_move(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float sum8(float x) {
-  x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
-  x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
-  x += dpp_move<0x141>(x);  // row_half_mirror: lane i <-> 7 - i of its 8
-  return x;
-}
 
 }  // namespace
 

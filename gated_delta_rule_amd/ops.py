@@ -187,6 +187,59 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     return out
 
 
+def decode_layer_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor, a: torch.Tensor,
+                      b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor, state: torch.Tensor,
+                      z: torch.Tensor, norm_w: torch.Tensor, num_k_heads: int, num_v_heads: int,
+                      state_indices: Optional[torch.Tensor] = None, use_qk_l2norm_in_kernel: bool = True,
+                      scale: float = 1.0, norm_eps: float = 1e-6, return_intermediates: bool = False):
+    """One decode token of the layer path in one launch (gdr_decode_layer_step):
+    conv front against the rolling ``conv_state``, gates, recurrent step, gated
+    RMS norm.  Both states are updated in place.
+
+    x: [N, C] bf16 (C = (2*Hk + Hv)*128, blocks q | k | v); conv_w: [C, 4] bf16;
+    conv_state: [P, C, 3] bf16; a, b: [N, Hv] fp32; A_log, dt_bias: [Hv] fp32;
+    state: [P, Hv, 128, 128] fp32; z: [N, Hv*128] bf16; norm_w: [128] fp32.
+    Without ``state_indices`` P = N and row n uses slot n; with it (int32 [N])
+    row n uses slot state_indices[n] of both pools, and an index outside [0, P)
+    marks a padding row (zero outputs, no slot touched).
+    Returns y [N, Hv*128] bf16, or (y, o [N, Hv, 128] fp32, qkv [N, C] bf16)
+    with ``return_intermediates``.
+    """
+    dev = x.device
+    Hk, Hv, D = num_k_heads, num_v_heads, 128
+    N, C = x.shape
+    if C != (2 * Hk + Hv) * D:
+        raise ValueError(f"x must be [N, {(2 * Hk + Hv) * D}]")
+    _need(x, "x", (torch.bfloat16,), dev)
+    _need(conv_w, "conv_w", (torch.bfloat16,), dev)
+    _need(conv_state, "conv_state", (torch.bfloat16,), dev)
+    _need(z, "z", (torch.bfloat16,), dev)
+    for t, name in ((a, "a"), (b, "b"), (A_log, "A_log"), (dt_bias, "dt_bias"), (state, "state"),
+                    (norm_w, "norm_w")):
+        _need(t, name, (torch.float32,), dev)
+    P = state.shape[0]
+    if conv_w.shape != (C, 4) or conv_state.shape != (P, C, 3) or state.shape != (P, Hv, D, D) \
+            or a.shape != (N, Hv) or b.shape != (N, Hv) or z.shape != (N, Hv * D) or norm_w.shape != (D,):
+        raise ValueError("shape mismatch among the decode-layer arguments")
+    if state_indices is None:
+        if P != N:
+            raise ValueError("without state_indices the pools hold one slot per row")
+    else:
+        _need(state_indices, "state_indices", (torch.int32,), dev)
+        if state_indices.shape != (N,):
+            raise ValueError(f"state_indices must be [{N}]")
+    y = torch.empty((N, Hv * D), device=dev, dtype=torch.bfloat16)
+    o = torch.empty((N, Hv, D), device=dev, dtype=torch.float32) if return_intermediates else None
+    qkv = torch.empty((N, C), device=dev, dtype=torch.bfloat16) if return_intermediates else None
+    desc = make_desc(N, 1, N, Hk, Hv, D, 64, torch.bfloat16, torch.float32, use_qk_l2norm_in_kernel, scale, 1e-6)
+    st = _lib.load().gdr_decode_layer_step(
+        ctypes.byref(desc), _ptr(x), _ptr(conv_w), _ptr(conv_state) if conv_state.numel() else None, _ptr(a),
+        _ptr(b), _ptr(A_log), _ptr(dt_bias), _ptr(state) if state.numel() else None, P, _ptr(state_indices),
+        _ptr(z), _ptr(norm_w), norm_eps, _ptr(y), _ptr(o), _ptr(qkv), _stream(dev))
+    _lib.check("gdr_decode_layer_step", st)
+    return (y, o, qkv) if return_intermediates else y
+
+
 def conv_gate_fused(x: torch.Tensor, conv_w: torch.Tensor, cu_seqlens: torch.Tensor, a: torch.Tensor,
                     b: torch.Tensor, A_log: torch.Tensor, dt_bias: torch.Tensor, num_k_heads: int,
                     num_v_heads: int, head_dim: int, conv_state_in: Optional[torch.Tensor] = None,

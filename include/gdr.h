@@ -205,6 +205,45 @@ gdr_status gdr_recurrent_step_indexed(const gdr_desc* d, const void* q, const vo
                                       void* stream);
 
 /*
+ * One decode token of the whole layer path in one launch: the conv front for
+ * the token against a rolling conv state, the gates, the recurrent step and
+ * the gated RMS norm (deepmagic page, architecture section: conv in front,
+ * gated RMS norm behind; yfxerp page, section 1.2: the decode path takes a
+ * single-step recurrence and keeps the conv state beside the recurrent
+ * state).  d->batch = N rows, d->seq_len = 1, d_k = d_v = 128, bf16 x,
+ * Hv/Hk in {1, 2, 3, 4}; d->scale, use_qk_l2norm and l2norm_eps as for
+ * gdr_recurrent_step.  C = (2*Hk + Hv) * 128.
+ *
+ *   x             [N, C] bf16: the token's projections, channel blocks q | k | v
+ *   conv_w        [C, 4] bf16 (8-byte aligned); tap 3 multiplies this token
+ *   conv_state    [P, C, 3] bf16, the three previous inputs of each channel,
+ *                 oldest first; rolled IN PLACE to end with this token
+ *   a, b          [N, Hv] fp32;  A_log, dt_bias [Hv] fp32 (the gates)
+ *   state         [P, Hv, 128, 128] fp32, updated IN PLACE
+ *   state_indices NULL: row n uses slot n of both pools (P = N); else [N]
+ *                 int32 device array naming each row's slot of both pools,
+ *                 pool_size slots each; an entry outside [0, pool_size) marks
+ *                 a padding row: its outputs are zeros and no slot is read or
+ *                 written.  The other entries must be distinct.
+ *   z             [N, Hv*128] bf16, the norm's gate input;  norm_w [128] fp32
+ *   y             [N, Hv*128] bf16 = o / sqrt(mean(o^2) + norm_eps) * norm_w
+ *                 * z * sigmoid(z) per (row, value head)
+ *   o             [N, Hv, 128] fp32 pre-norm outputs, or NULL (not written)
+ *   qkv_out       [N, C] bf16 conv + SiLU outputs, or NULL (not written)
+ *
+ * The conv output is bit-identical to gdr_conv_gate_fused on the same token
+ * and state; o and the new state are bit-identical to gdr_recurrent_step on
+ * that front's q, k, v, g and beta.  Errors: INVALID_ARG for a NULL required
+ * pointer, misalignment, pool_size < 0, seq_len != 1; UNSUPPORTED for other
+ * head sizes or ratios or a non-bf16 x.
+ */
+gdr_status gdr_decode_layer_step(const gdr_desc* d, const void* x, const void* conv_w, void* conv_state,
+                                 const float* a, const float* b, const float* A_log, const float* dt_bias,
+                                 float* state, int32_t pool_size, const int32_t* state_indices,
+                                 const void* z, const float* norm_w, float norm_eps, void* y, float* o,
+                                 void* qkv_out, void* stream);
+
+/*
  * Front of the layer: depthwise causal conv (kernel 4, no bias) + SiLU over
  * all C = 2*Hk*d + Hv*d channels, plus the gates (deepmagic page: kernel-4
  * causal conv in front; yfxerp page, section 1.2: beta = sigmoid(b),

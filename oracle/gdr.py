@@ -51,6 +51,7 @@ __all__ = [
     "forward_parallel",
     "decode_step",
     "decode_step_pool",
+    "decode_layer_step",
     "chunked",
 ]
 
@@ -230,6 +231,48 @@ def decode_step_pool(q, k, v, g, beta, pool, state_indices, *, use_qk_l2norm: bo
         o[rows] = o_live
         new_pool[idx[rows]] = s_live
     return o, new_pool
+
+
+def decode_layer_step(x, conv_w, conv_state, a, b, A_log, dt_bias, state, z, norm_w, hk, hv, *,
+                      state_indices=None, use_qk_l2norm: bool = True, eps: float = 1e-6, scale: float = 1.0,
+                      norm_eps: float = 1e-6):
+    """One decode token of the layer path: the conv front against each row's
+    conv state (the fp32 bit-exact definition), the gates, decode_step_pool,
+    and the gated RMS norm (deepmagic page, architecture section; yfxerp page,
+    section 1.2: the decode path keeps a conv state beside the recurrent state).
+
+    x: [N, C] (C = (2 hk + hv) d, blocks q | k | v); conv_state: [P, C, 3];
+    state: [P, hv, d, d]; a, b: [N, hv]; z: [N, hv d].  Rows name slots of both
+    pools through state_indices (default: row n -> slot n); padding rows
+    (index outside [0, P)) give zero outputs and touch no slot.
+    Returns (y [N, hv d], o [N, hv, d], qkv [N, C] (bf16 values), new conv
+    pool, new state pool); y and o float64.
+    """
+    from oracle import conv as cv
+    x = np.asarray(x, dtype=np.float32)
+    N, C = x.shape
+    d = C // (2 * hk + hv)
+    P = len(state)
+    idx = np.arange(N) if state_indices is None else np.asarray(state_indices, dtype=np.int64)
+    live = np.flatnonzero((idx >= 0) & (idx < P))
+    conv_pool = np.array(conv_state, dtype=np.float32, copy=True)
+    qkv = np.zeros((N, C), dtype=np.float32)
+    if len(live):
+        cu = np.arange(len(live) + 1)
+        cs = conv_pool[idx[live]]
+        qkv[live] = cv.conv_silu_fp32(x[live], conv_w, cu, cs)
+        conv_pool[idx[live]] = cv.conv_state_out(x[live], cu, cs)
+    q = qkv[:, :hk * d].reshape(N, hk, d)
+    k = qkv[:, hk * d:2 * hk * d].reshape(N, hk, d)
+    v = qkv[:, 2 * hk * d:].reshape(N, hv, d)
+    g, beta = cv.gates(a, b, A_log, dt_bias)
+    o, new_state = decode_step_pool(q, k, v, g, beta, state, idx, use_qk_l2norm=use_qk_l2norm, eps=eps,
+                                    scale=scale)
+    y = np.zeros((N, hv * d))
+    if len(live):
+        zz = np.asarray(z, dtype=np.float64).reshape(N, hv, d)
+        y[live] = cv.gated_rmsnorm(o[live], zz[live], norm_w, norm_eps).reshape(len(live), hv * d)
+    return y, o, qkv, conv_pool, new_state
 
 
 def chunked(q, k, v, g, beta, initial_state=None, cu_seqlens=None, *, chunk_size: int = 64,

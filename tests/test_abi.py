@@ -129,6 +129,26 @@ def test_recurrent_step_validation():
     assert ix(ctypes.byref(_desc(batch=4, num_seqs=4, seq_len=2)), *args, FAKE, 8, FAKE, FAKE, None) == -1
 
 
+def test_decode_layer_step_validation():
+    lib = _lib.load()
+    f = lib.gdr_decode_layer_step
+    d = _desc(batch=4, num_seqs=4, seq_len=1)
+
+    def call(desc, state=FAKE, pool=8, x=FAKE, conv_w=FAKE):
+        return f(ctypes.byref(desc), x, conv_w, FAKE, FAKE, FAKE, FAKE, FAKE, state, pool, FAKE, FAKE, FAKE, 1e-6,
+                 FAKE, None, None, None)
+
+    assert call(_desc(batch=4, num_seqs=4, seq_len=2)) == -1
+    assert call(_desc(batch=4, num_seqs=4, seq_len=1, head_dim_k=64, head_dim_v=64)) == -2
+    assert call(_desc(batch=4, num_seqs=4, seq_len=1, num_k_heads=1, num_v_heads=5)) == -2
+    assert call(_desc(batch=4, num_seqs=4, seq_len=1, qkv_dtype=0)) == -2
+    assert call(d, pool=-1) == -1 and "pool_size" in lib.gdr_last_error().decode()
+    assert call(d, x=None) == -1
+    assert call(d, state=FAKE + 4) == -1 and "aligned" in lib.gdr_last_error().decode()
+    assert call(d, conv_w=FAKE + 2) == -1
+    assert call(_desc(batch=0, num_seqs=0, seq_len=1)) == 0  # nothing to do
+
+
 def test_conv_and_norm_validation():
     lib = _lib.load()
     c = _lib.GdrConvDesc()

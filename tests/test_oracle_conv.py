@@ -176,3 +176,45 @@ def test_gated_rmsnorm_properties():
     tiny = np.full((1, 16), 1e-4)
     yt = conv.gated_rmsnorm(tiny, np.full((1, 16), 50.0), np.ones(16), eps=1e-6)
     np.testing.assert_allclose(yt, 50.0 * 1e-4 / np.sqrt(1e-8 + 1e-6), rtol=1e-13)
+
+
+def test_decode_layer_steps_equal_prefill_definitions():
+    """Four chained decode-layer steps from zero conv and recurrent state equal,
+    token for token, the prefill definitions on the 4-token sequences: the conv
+    front (bit for bit), the recurrence on its outputs, and the gated norm; the
+    conv pool ends holding each row's last three inputs, slots by index."""
+    from oracle import gdr
+    cref = conv
+    r = np.random.default_rng(40)
+    N, hk, hv, d, T, P = 3, 1, 2, 8, 4, 5
+    C = (2 * hk + hv) * d
+    idx = np.array([4, 0, 2])
+    x = cref.round_bf16(r.standard_normal((N, T, C)))
+    w = cref.round_bf16(r.uniform(-0.5, 0.5, (C, 4)))
+    a = r.standard_normal((N, T, hv))
+    b = r.standard_normal((N, T, hv))
+    A_log, dt = r.uniform(0, 1, hv), r.uniform(-1, 1, hv)
+    z = r.standard_normal((N, T, hv * d))
+    nw = 1 + 0.1 * r.standard_normal(d)
+    conv_pool = np.zeros((P, C, 3), np.float32)
+    pool = np.zeros((P, hv, d, d))
+    ys, os_, qkvs = [], [], []
+    for t in range(T):
+        y, o, qkv, conv_pool, pool = gdr.decode_layer_step(x[:, t], w, conv_pool, a[:, t], b[:, t], A_log, dt, pool,
+                                                           z[:, t], nw, hk, hv, state_indices=idx)
+        ys.append(y), os_.append(o), qkvs.append(qkv)
+    cu = np.arange(0, N * T + 1, T)
+    flat = x.reshape(N * T, C)
+    conv_ref = cref.conv_silu_fp32(flat, w, cu).reshape(N, T, C)
+    assert np.array_equal(np.stack(qkvs, 1), conv_ref)
+    assert np.array_equal(conv_pool[idx], cref.conv_state_out(flat, cu))
+    q = conv_ref[..., :hk * d].reshape(N, T, hk, d)
+    k = conv_ref[..., hk * d:2 * hk * d].reshape(N, T, hk, d)
+    v = conv_ref[..., 2 * hk * d:].reshape(N, T, hv, d)
+    g, beta = cref.gates(a, b, A_log, dt)
+    o_ref, s_ref = gdr.forward(q, k, v, g, beta)
+    np.testing.assert_allclose(np.stack(os_, 1), o_ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(pool[idx], s_ref, rtol=1e-12, atol=1e-14)
+    y_ref = cref.gated_rmsnorm(o_ref, z.reshape(N, T, hv, d), nw).reshape(N, T, hv * d)
+    np.testing.assert_allclose(np.stack(ys, 1), y_ref, rtol=1e-12, atol=1e-14)
+    assert np.all(pool[[1, 3]] == 0) and np.all(conv_pool[[1, 3]] == 0)
