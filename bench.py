@@ -11,6 +11,9 @@ in the same run:
 
   decode    -- 64 sequences x 48 heads of 128x128 fp32 state, one token per
                step, state updated in place, 256 steps: state GB/s
+  decode_layer -- one token of the whole layer path for the same 64
+               sequences in one launch (conv front, gates, recurrent step,
+               gated RMS norm), beside the same work as three launches
   pipeline  -- the whole layer path over a packed batch of 8 sequences
                (65536 tokens): conv+SiLU+gates, recurrence, gated RMSNorm
   roofline  -- the dominant kernel of the call, the state-carrying
@@ -29,7 +32,7 @@ in the same run:
                and 4 decode steps for the decode leg)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pieces P] [--no-cpu]
-                       [--only prefill|decode|pipeline|copy|roofline|all]
+                       [--only prefill|decode|decode_layer|pipeline|copy|roofline|all]
 """
 from __future__ import annotations
 
@@ -420,7 +423,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=24)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "pipeline", "copy", "roofline"])
+    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "decode_layer", "pipeline", "copy",
+                                                      "roofline"])
     ap.add_argument("--pieces", type=int, default=N_CALLS,
                     help="distinct 32K pieces of the context to cycle through (8 = the whole 262144 tokens)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -494,6 +498,8 @@ def main():
             out["decode_2_replicas"] = bench_decode(replicas=2)
             out["decode_pool_indexed"] = bench_decode(pool=128)
             out["decode_layer"] = bench_decode_layer()
+    if args.only == "decode_layer":
+        out["decode_layer"] = bench_decode_layer()
     if args.only in ("all", "pipeline"):
         out["pipeline"] = bench_pipeline()
     if args.only == "all":
