@@ -10,7 +10,10 @@ from .ops import (  # noqa: F401
     chunk_workspace,
     conv_gate_fused,
     decode_layer_step,
+    delta_layer_fwd,
+    delta_layer_workspace,
     gated_rmsnorm,
+    linear,
     recurrent_step,
 )
 
@@ -23,4 +26,7 @@ __all__ = [
     "decode_layer_step",
     "conv_gate_fused",
     "gated_rmsnorm",
+    "linear",
+    "delta_layer_fwd",
+    "delta_layer_workspace",
 ]

@@ -27,6 +27,9 @@ EXPORTED = (
     "gdr_decode_layer_step",
     "gdr_conv_gate_fused",
     "gdr_gated_rmsnorm",
+    "gdr_linear",
+    "gdr_delta_layer_workspace_size",
+    "gdr_delta_layer_fwd",
 )
 
 
@@ -68,6 +71,31 @@ class GdrNormDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("o_dtype", ctypes.c_int32),
         ("eps", ctypes.c_float),
+    ]
+
+
+class GdrLinearOut(ctypes.Structure):
+    _fields_ = [
+        ("ptr", ctypes.c_void_p),
+        ("ld", ctypes.c_int64),
+        ("cols", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("round_bf16", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class GdrLayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("num_tokens", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("num_k_heads", ctypes.c_int32),
+        ("num_v_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("l2norm_eps", ctypes.c_float),
+        ("norm_eps", ctypes.c_float),
     ]
 
 
@@ -116,6 +144,14 @@ def load() -> ctypes.CDLL:
     lib.gdr_conv_gate_fused.argtypes = [ctypes.POINTER(GdrConvDesc)] + [P] * 15
     lib.gdr_gated_rmsnorm.restype = I32
     lib.gdr_gated_rmsnorm.argtypes = [ctypes.POINTER(GdrNormDesc), P, P, P, P, P]
+    I64 = ctypes.c_int64
+    lib.gdr_linear.restype = I32
+    lib.gdr_linear.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, I64, P, I64,
+                               ctypes.POINTER(GdrLinearOut), ctypes.c_int32, P]
+    lib.gdr_delta_layer_workspace_size.restype = I32
+    lib.gdr_delta_layer_workspace_size.argtypes = [ctypes.POINTER(GdrLayerDesc), ctypes.POINTER(SZ)]
+    lib.gdr_delta_layer_fwd.restype = I32
+    lib.gdr_delta_layer_fwd.argtypes = [ctypes.POINTER(GdrLayerDesc)] + [P] * 14 + [SZ, P]
     _lib = lib
     return lib
 

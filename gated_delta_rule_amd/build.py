@@ -30,6 +30,7 @@ SOURCES = [
     "kernels/chunk_bf16.hip",
     "kernels/conv_front.hip",
     "kernels/gated_rmsnorm.hip",
+    "kernels/linear_bf16.hip",
 ]
 ROOFLINE_SOURCES = ["roofline/roofline.hip"]
 
@@ -54,10 +55,18 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libgdr)")
 
 
+# The GEMM keeps its 256 accumulators per lane in the accumulation
+# registers, so it is built without the VGPR form.
+NO_VGPR_FORM = {"kernels/linear_bf16.hip"}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, src.replace("/", "_") + ".o")
     lang = ["-x", "hip"]
-    cmd = [_hipcc(), *lang, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    flags = FLAGS
+    if src in NO_VGPR_FORM:
+        flags = [f for f in FLAGS if f not in ("-mllvm", "-amdgpu-mfma-vgpr-form=1")]
+    cmd = [_hipcc(), *lang, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

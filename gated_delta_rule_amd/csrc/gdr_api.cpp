@@ -356,4 +356,184 @@ gdr_status gdr_gated_rmsnorm(const gdr_norm_desc* d, const void* o, const void* 
   return hip_status(gdr::launch_gated_rmsnorm(n, static_cast<hipStream_t>(stream)), "gdr_gated_rmsnorm launch");
 }
 
+gdr_status gdr_linear(int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx, const void* w, int64_t ldw,
+                      const gdr_linear_out* outs, int32_t num_outs, void* stream) {
+  if (M < 0 || N < 0 || K <= 0) return fail(GDR_ERR_INVALID_ARG, "need M, N >= 0 and K > 0 (got %d, %d, %d)", M, N, K);
+  if (K % 128) return fail(GDR_ERR_INVALID_ARG, "K (%d) must be a multiple of 128", K);
+  if (ldx < K || ldw < K || ldx % 8 || ldw % 8)
+    return fail(GDR_ERR_INVALID_ARG, "ldx and ldw must be >= K and multiples of 8");
+  if (!outs || num_outs < 1 || num_outs > 4) return fail(GDR_ERR_INVALID_ARG, "need 1..4 output blocks");
+  const bool work = M > 0 && N > 0;
+  if (work && (!x || !w)) return fail(GDR_ERR_INVALID_ARG, "x and w are required");
+  if (!aligned16(x) || !aligned16(w)) return fail(GDR_ERR_INVALID_ARG, "x and w must be 16-byte aligned");
+  gdr::LinearArgs a{};
+  a.x = x;
+  a.w = w;
+  a.ldx = ldx;
+  a.ldw = ldw;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.nout = num_outs;
+  int64_t col = 0;
+  for (int i = 0; i < num_outs; ++i) {
+    const gdr_linear_out& o = outs[i];
+    if (o.cols < 0 || o.ld < o.cols) return fail(GDR_ERR_INVALID_ARG, "output block %d: need 0 <= width <= ld", i);
+    if (o.dtype != GDR_BF16 && o.dtype != GDR_F32) return fail(GDR_ERR_INVALID_ARG, "output block %d: bad dtype", i);
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(o.ptr);
+    const unsigned elem = o.dtype == GDR_BF16 ? 2u : 4u;
+    if (M > 0 && o.cols > 0 && !o.ptr) return fail(GDR_ERR_INVALID_ARG, "output block %d is NULL", i);
+    if (addr % elem) return fail(GDR_ERR_INVALID_ARG, "output block %d must be %u-byte aligned", i, elem);
+    a.out[i].ptr = o.ptr;
+    a.out[i].ld = o.ld;
+    a.out[i].n0 = (int)col;
+    a.out[i].n1 = (int)(col + o.cols);
+    a.out[i].kind = o.dtype == GDR_BF16 ? gdr::kLinearBf16 : o.round_bf16 ? gdr::kLinearF32Bf16 : gdr::kLinearF32;
+    a.out[i].vec = col % 4 == 0 && o.ld % 4 == 0 && addr % (4u * elem) == 0;
+    col += o.cols;
+  }
+  if (col != N) return fail(GDR_ERR_INVALID_ARG, "output block widths sum to %lld, N is %d", (long long)col, N);
+  // An empty block starts where the next one does, so routing by first column
+  // never picks it.
+  return hip_status(gdr::launch_linear(a, static_cast<hipStream_t>(stream)), "gdr_linear launch");
+}
+
+namespace {
+
+// Intermediates of gdr_delta_layer_fwd, 256-byte aligned pieces of the workspace.
+struct LayerBufs {
+  size_t qkv, z, b, a, q, k, v, g, beta, o, chunk, total, chunk_bytes;
+};
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+gdr_desc layer_chunk_desc(const gdr_layer_desc* d) {
+  gdr_desc c{};
+  c.struct_size = sizeof(gdr_desc);
+  c.batch = 1;
+  c.seq_len = d->num_tokens;
+  c.num_seqs = d->num_seqs;
+  c.num_k_heads = d->num_k_heads;
+  c.num_v_heads = d->num_v_heads;
+  c.head_dim_k = c.head_dim_v = d->head_dim;
+  c.chunk_size = 64;
+  c.qkv_dtype = GDR_BF16;
+  c.out_dtype = GDR_F32;
+  c.use_qk_l2norm = 1;
+  c.scale = 1.f;
+  c.l2norm_eps = d->l2norm_eps;
+  return c;
+}
+
+gdr_status layer_plan(const gdr_layer_desc* d, LayerBufs* p) {
+  if (!d) return fail(GDR_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->struct_size < sizeof(gdr_layer_desc))
+    return fail(GDR_ERR_INVALID_ARG, "descriptor struct_size %u < %zu", d->struct_size, sizeof(gdr_layer_desc));
+  if (d->num_tokens < 0 || d->num_seqs < 1 || d->num_k_heads <= 0 || d->num_v_heads <= 0 || d->hidden <= 0)
+    return fail(GDR_ERR_INVALID_ARG, "need num_tokens >= 0, num_seqs >= 1, positive heads and hidden");
+  if (d->num_v_heads % d->num_k_heads)
+    return fail(GDR_ERR_INVALID_ARG, "num_v_heads must be a multiple of num_k_heads");
+  if (d->head_dim != 128) return fail(GDR_ERR_UNSUPPORTED, "the delta layer takes head_dim 128 (got %d)", d->head_dim);
+  if (d->hidden % 128) return fail(GDR_ERR_INVALID_ARG, "hidden (%d) must be a multiple of 128", d->hidden);
+  if (!(d->l2norm_eps >= 0.f) || !(d->norm_eps >= 0.f)) return fail(GDR_ERR_INVALID_ARG, "eps must be >= 0");
+  const size_t T = (size_t)d->num_tokens, Hk = d->num_k_heads, Hv = d->num_v_heads, D = d->head_dim;
+  const size_t C = (2 * Hk + Hv) * D, V = Hv * D;
+  const gdr_desc cd = layer_chunk_desc(d);
+  size_t cb = 0;
+  const gdr_status st = gdr_chunk_fwd_workspace_size(&cd, &cb);
+  if (st != GDR_OK) return st;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += up256(bytes);
+    return at;
+  };
+  p->qkv = take(T * C * 2);  // reused for y once the front has read it
+  p->z = take(T * V * 2);
+  p->b = take(T * Hv * 4);
+  p->a = take(T * Hv * 4);
+  p->q = take(T * Hk * D * 2);
+  p->k = take(T * Hk * D * 2);
+  p->v = take(T * V * 2);
+  p->g = take(T * Hv * 4);
+  p->beta = take(T * Hv * 4);
+  p->o = take(T * V * 4);
+  p->chunk = take(cb);
+  p->chunk_bytes = cb;
+  p->total = off;
+  return ok();
+}
+
+}  // namespace
+
+gdr_status gdr_delta_layer_workspace_size(const gdr_layer_desc* d, size_t* bytes) {
+  if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+  LayerBufs p;
+  const gdr_status st = layer_plan(d, &p);
+  if (st != GDR_OK) return st;
+  *bytes = p.total;
+  return ok();
+}
+
+gdr_status gdr_delta_layer_fwd(const gdr_layer_desc* d, const void* hidden, const void* w_in, const void* conv_w,
+                               const float* A_log, const float* dt_bias, const float* norm_w, const void* w_out,
+                               const int32_t* cu_seqlens, const void* conv_state_in, void* conv_state_out,
+                               const float* initial_state, float* final_state, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  LayerBufs p;
+  gdr_status st = layer_plan(d, &p);
+  if (st != GDR_OK) return st;
+  if (!hidden || !w_in || !conv_w || !A_log || !dt_bias || !norm_w || !w_out || !cu_seqlens || !out)
+    return fail(GDR_ERR_INVALID_ARG, "hidden, w_in, conv_w, A_log, dt_bias, norm_w, w_out, cu_seqlens and out are required");
+  if (!workspace || workspace_bytes < p.total)
+    return fail(GDR_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", p.total, workspace ? workspace_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GDR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int T = d->num_tokens, H = d->hidden, Hk = d->num_k_heads, Hv = d->num_v_heads, D = d->head_dim;
+  const int C = (2 * Hk + Hv) * D, V = Hv * D;
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  void* qkv = ws + p.qkv;
+  void* z = ws + p.z;
+  float* bb = reinterpret_cast<float*>(ws + p.b);
+  float* aa = reinterpret_cast<float*>(ws + p.a);
+  void* q = ws + p.q;
+  void* k = ws + p.k;
+  void* v = ws + p.v;
+  float* g = reinterpret_cast<float*>(ws + p.g);
+  float* beta = reinterpret_cast<float*>(ws + p.beta);
+  float* o = reinterpret_cast<float*>(ws + p.o);
+  void* y = qkv;
+
+  gdr_linear_out in_outs[4] = {
+      {qkv, C, C, GDR_BF16, 0, 0}, {z, V, V, GDR_BF16, 0, 0}, {bb, Hv, Hv, GDR_F32, 1, 0}, {aa, Hv, Hv, GDR_F32, 1, 0}};
+  if ((st = gdr_linear(T, C + V + 2 * Hv, H, hidden, H, w_in, H, in_outs, 4, stream)) != GDR_OK) return st;
+
+  gdr_conv_desc cd{};
+  cd.struct_size = sizeof(cd);
+  cd.num_tokens = T;
+  cd.num_seqs = d->num_seqs;
+  cd.num_k_heads = Hk;
+  cd.num_v_heads = Hv;
+  cd.head_dim = D;
+  if ((st = gdr_conv_gate_fused(&cd, qkv, conv_w, cu_seqlens, conv_state_in, conv_state_out, aa, bb, A_log, dt_bias,
+                                q, k, v, g, beta, stream)) != GDR_OK)
+    return st;
+
+  const gdr_desc rd = layer_chunk_desc(d);
+  if ((st = gdr_chunk_fwd(&rd, q, k, v, g, beta, initial_state, final_state, cu_seqlens, o, ws + p.chunk,
+                          p.chunk_bytes, stream)) != GDR_OK)
+    return st;
+
+  gdr_norm_desc nd{};
+  nd.struct_size = sizeof(nd);
+  nd.num_tokens = T;
+  nd.num_heads = Hv;
+  nd.head_dim = D;
+  nd.o_dtype = GDR_F32;
+  nd.eps = d->norm_eps;
+  if ((st = gdr_gated_rmsnorm(&nd, o, z, norm_w, y, stream)) != GDR_OK) return st;
+
+  gdr_linear_out out_blk = {out, H, H, GDR_BF16, 0, 0};
+  return gdr_linear(T, H, V, y, V, w_out, V, &out_blk, 1, stream);
+}
+
 }  // extern "C"

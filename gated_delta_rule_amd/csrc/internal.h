@@ -71,7 +71,29 @@ struct NormArgs {
   float eps;
 };
 
+// y = x W^T (bf16 operands, fp32 accumulation); output columns are split into
+// up to four blocks, each written to its own buffer.
+constexpr int kLinearBf16 = 0;     // bf16, round to nearest even
+constexpr int kLinearF32 = 1;      // fp32 accumulator
+constexpr int kLinearF32Bf16 = 2;  // fp32 holding the bf16-rounded value
+struct LinearOut {
+  void* ptr;
+  int64_t ld;  // row stride in elements
+  int n0, n1;  // output columns [n0, n1) of the block
+  int kind;    // kLinear*
+  int vec;     // n0 and ld multiples of 4 and ptr 8 (bf16) / 16 (fp32) byte aligned
+};
+struct LinearArgs {
+  const void* x;  // [M, K] bf16, row stride ldx
+  const void* w;  // [N, K] bf16, row stride ldw
+  int64_t ldx, ldw;
+  int M, N, K;    // K a multiple of 128
+  int nout;       // 1..4 blocks, contiguous, out[0].n0 = 0, empty ones allowed
+  LinearOut out[4];
+};
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_linear(const LinearArgs& a, hipStream_t st);
 hipError_t launch_decode_layer(const LayerStepArgs& a, hipStream_t st);
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t st);
 // The bf16-MFMA prefill needs a device workspace of

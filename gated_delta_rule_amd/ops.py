@@ -312,3 +312,114 @@ def gated_rmsnorm(o: torch.Tensor, z: torch.Tensor, w: torch.Tensor, eps: float 
     st = _lib.load().gdr_gated_rmsnorm(ctypes.byref(desc), _ptr(o), _ptr(z), _ptr(w), _ptr(out), _stream(dev))
     _lib.check("gdr_gated_rmsnorm", st)
     return out
+
+
+def linear(x: torch.Tensor, w: torch.Tensor, blocks=None, out_dtype: torch.dtype = torch.bfloat16):
+    """Dense projection y = x W^T (gdr_linear): bf16 operands, fp32 accumulation.
+
+    x: [M, K] bf16, w: [N, K] bf16 (K a multiple of 128).  Without ``blocks``
+    returns one [M, N] tensor of ``out_dtype`` (bf16 or fp32).  ``blocks`` is a
+    list of (width, dtype) or (width, dtype, round_bf16) splitting the N output
+    columns into separate tensors, returned as a list.
+    """
+    dev = x.device
+    _need(x, "x", (torch.bfloat16,), dev)
+    _need(w, "w", (torch.bfloat16,), dev)
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError("x must be [M, K] and w [N, K]")
+    M, K = x.shape
+    N = w.shape[0]
+    single = blocks is None
+    if single:
+        blocks = [(N, out_dtype)]
+    if not 1 <= len(blocks) <= 4:
+        raise ValueError("1..4 output blocks")
+    outs = (_lib.GdrLinearOut * len(blocks))()
+    tensors = []
+    for i, blk in enumerate(blocks):
+        width, dt = blk[0], blk[1]
+        rnd = bool(blk[2]) if len(blk) > 2 else False
+        t = torch.empty((M, width), device=dev, dtype=dt)
+        tensors.append(t)
+        outs[i].ptr = t.data_ptr() if t.numel() else None
+        outs[i].ld = width
+        outs[i].cols = width
+        outs[i].dtype = _DT[dt]
+        outs[i].round_bf16 = int(rnd)
+        outs[i].reserved = 0
+    st = _lib.load().gdr_linear(M, N, K, _ptr(x), K, _ptr(w), K, outs, len(blocks), _stream(dev))
+    _lib.check("gdr_linear", st)
+    return tensors[0] if single else tensors
+
+
+def layer_desc(T, N, hidden, Hk, Hv, D, l2norm_eps=1e-6, norm_eps=1e-6):
+    d = _lib.GdrLayerDesc()
+    d.struct_size = ctypes.sizeof(_lib.GdrLayerDesc)
+    d.num_tokens, d.num_seqs, d.hidden = T, N, hidden
+    d.num_k_heads, d.num_v_heads, d.head_dim = Hk, Hv, D
+    d.l2norm_eps, d.norm_eps = l2norm_eps, norm_eps
+    return d
+
+
+def delta_layer_workspace(T: int, N: int, hidden: int, num_k_heads: int, num_v_heads: int, head_dim: int = 128,
+                          device=None) -> torch.Tensor:
+    """A device workspace large enough for delta_layer_fwd on these sizes."""
+    d = layer_desc(T, N, hidden, num_k_heads, num_v_heads, head_dim)
+    n = ctypes.c_size_t(0)
+    _lib.check("gdr_delta_layer_workspace_size", _lib.load().gdr_delta_layer_workspace_size(ctypes.byref(d),
+                                                                                           ctypes.byref(n)))
+    return torch.empty(max(n.value, 1), device=device, dtype=torch.uint8)
+
+
+def delta_layer_fwd(hidden: torch.Tensor, w_in: torch.Tensor, conv_w: torch.Tensor, A_log: torch.Tensor,
+                    dt_bias: torch.Tensor, norm_w: torch.Tensor, w_out: torch.Tensor, cu_seqlens: torch.Tensor,
+                    num_k_heads: int, num_v_heads: int, head_dim: int = 128,
+                    conv_state_in: Optional[torch.Tensor] = None, output_conv_state: bool = False,
+                    initial_state: Optional[torch.Tensor] = None, output_final_state: bool = False,
+                    final_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, l2norm_eps: float = 1e-6, norm_eps: float = 1e-6):
+    """Prefill of one whole delta layer (gdr_delta_layer_fwd).
+
+    hidden: [T, H] bf16; w_in: [C + V + 2*Hv, H] bf16 (rows q|k|v, z, b, a);
+    conv_w: [C, 4] bf16; A_log, dt_bias: [Hv] fp32; norm_w: [d] fp32;
+    w_out: [H, V] bf16; cu_seqlens: int32 [N+1].
+    Returns (out [T, H] bf16, final_state or None, conv_state_out or None).
+    """
+    dev = hidden.device
+    Hk, Hv, D = num_k_heads, num_v_heads, head_dim
+    T, H = hidden.shape
+    C, V = (2 * Hk + Hv) * D, Hv * D
+    _need(hidden, "hidden", (torch.bfloat16,), dev)
+    _need(w_in, "w_in", (torch.bfloat16,), dev)
+    _need(conv_w, "conv_w", (torch.bfloat16,), dev)
+    _need(w_out, "w_out", (torch.bfloat16,), dev)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,), dev)
+    for t, name in ((A_log, "A_log"), (dt_bias, "dt_bias"), (norm_w, "norm_w")):
+        _need(t, name, (torch.float32,), dev)
+    N = cu_seqlens.numel() - 1
+    if w_in.shape != (C + V + 2 * Hv, H) or w_out.shape != (H, V) or conv_w.shape != (C, 4) \
+            or A_log.shape != (Hv,) or dt_bias.shape != (Hv,) or norm_w.shape != (D,):
+        raise ValueError("shape mismatch in delta layer weights")
+    if conv_state_in is not None:
+        _need(conv_state_in, "conv_state_in", (torch.bfloat16,), dev)
+        if conv_state_in.shape != (N, C, 3):
+            raise ValueError(f"conv_state_in must be {(N, C, 3)}")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (torch.float32,), dev)
+        if initial_state.shape != (N, Hv, D, D):
+            raise ValueError(f"initial_state must be {(N, Hv, D, D)}")
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, Hv, D, D), device=dev, dtype=torch.float32)
+    conv_state_out = torch.empty((N, C, 3), device=dev, dtype=torch.bfloat16) if output_conv_state else None
+    if out is None:
+        out = torch.empty((T, H), device=dev, dtype=torch.bfloat16)
+    d = layer_desc(T, N, H, Hk, Hv, D, l2norm_eps, norm_eps)
+    if workspace is None:
+        workspace = delta_layer_workspace(T, N, H, Hk, Hv, D, device=dev)
+    st = _lib.load().gdr_delta_layer_fwd(ctypes.byref(d), _ptr(hidden), _ptr(w_in), _ptr(conv_w), _ptr(A_log),
+                                         _ptr(dt_bias), _ptr(norm_w), _ptr(w_out), _ptr(cu_seqlens),
+                                         _ptr(conv_state_in), _ptr(conv_state_out), _ptr(initial_state),
+                                         _ptr(final_state), _ptr(out), _ptr(workspace), workspace.numel(),
+                                         _stream(dev))
+    _lib.check("gdr_delta_layer_fwd", st)
+    return out, final_state, conv_state_out

@@ -42,6 +42,10 @@ __all__ = [
     "decode_step_inputs",
     "varlen_lengths",
     "pipeline_inputs",
+    "matmul_inputs",
+    "LayerInputs",
+    "layer_inputs",
+    "HIDDEN",
     "HK",
     "HV",
     "D",
@@ -247,3 +251,52 @@ def pipeline_inputs(seed: int = 5, *, lengths=None, hk: int = HK, hv: int = HV, 
     z = round_bf16(gen.standard_normal((T, hv * d), dtype=np.float32))
     norm_w = (1.0 + 0.1 * gen.standard_normal(d)).astype(np.float32)
     return PipelineInputs(x, conv_w, a, b, A_log, dt_bias, z, norm_w, cu, hk, hv, d)
+
+
+HIDDEN = 5120  # model width of the pages' layer
+
+
+def matmul_inputs(seed: int, M: int, N: int, K: int):
+    """x [M, K] ~ N(0, 1) and w [N, K] ~ N(0, 1/K), both bf16 values (float32 arrays)."""
+    gen = rng(seed, 20)
+    x = round_bf16(gen.standard_normal((M, K), dtype=np.float32))
+    w = round_bf16(gen.standard_normal((N, K), dtype=np.float32) / np.float32(math.sqrt(K)))
+    return x, w
+
+
+@dataclass
+class LayerInputs:
+    hidden: np.ndarray   # [T, H] bf16 values
+    w_in: np.ndarray     # [C + V + 2 hv, H] bf16 values: rows q|k|v, z, b, a
+    conv_w: np.ndarray   # [C, 4] bf16 values
+    A_log: np.ndarray    # [hv]
+    dt_bias: np.ndarray  # [hv]
+    norm_w: np.ndarray   # [d]
+    w_out: np.ndarray    # [H, V] bf16 values
+    cu_seqlens: np.ndarray
+    hk: int
+    hv: int
+    d: int
+
+
+def layer_inputs(seed: int = 6, *, lengths=(4096,), hk: int = HK, hv: int = HV, d: int = D,
+                 hidden: int = HIDDEN) -> LayerInputs:
+    """Synthetic weights and activations of one whole delta layer.
+
+    hidden ~ N(0, 1); projection weights ~ N(0, 1/fan_in), so every projection
+    output is about N(0, 1) like the activations the path recipe draws; conv
+    weights ~ U(-0.5, 0.5), per-head A_log / dt_bias as in the path recipe,
+    norm weight 1 + 0.1 N(0, 1).  No trained values are involved.
+    """
+    cu = cu_seqlens_of(list(lengths))
+    T = int(cu[-1])
+    C, V = (2 * hk + hv) * d, hv * d
+    A_log, dt_bias = _head_params(rng(seed, 0), hv)
+    gen = rng(seed, 21)
+    x = round_bf16(gen.standard_normal((T, hidden), dtype=np.float32))
+    w_in = round_bf16(gen.standard_normal((C + V + 2 * hv, hidden), dtype=np.float32)
+                      / np.float32(math.sqrt(hidden)))
+    conv_w = round_bf16(gen.uniform(-0.5, 0.5, size=(C, 4)))
+    norm_w = (1.0 + 0.1 * gen.standard_normal(d)).astype(np.float32)
+    w_out = round_bf16(gen.standard_normal((hidden, V), dtype=np.float32) / np.float32(math.sqrt(V)))
+    return LayerInputs(x, w_in, conv_w, A_log, dt_bias, norm_w, w_out, cu, hk, hv, d)

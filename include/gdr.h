@@ -288,6 +288,98 @@ gdr_status gdr_conv_gate_fused(const gdr_conv_desc* d, const void* x, const void
 gdr_status gdr_gated_rmsnorm(const gdr_norm_desc* d, const void* o, const void* z,
                              const float* w, void* y, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The delta layer around the path: its dense projections and the whole layer
+ * prefill (deepmagic page, parameter table: per delta-rule layer a q|k|v
+ * projection, a z projection 6144 wide, b and a projections 48 wide each
+ * and an output projection from 6144; architecture section: hidden width
+ * 5120).  The weights are the caller's; nothing here depends on trained
+ * values.
+ * ------------------------------------------------------------------------ */
+
+/* One block of output columns of gdr_linear. */
+typedef struct gdr_linear_out {
+  void* ptr;          /* device [M, cols] with row stride ld, aligned to its element */
+  int64_t ld;         /* row stride in elements, >= cols */
+  int32_t cols;       /* block width (0 allowed) */
+  int32_t dtype;      /* GDR_BF16 (round to nearest even) or GDR_F32 */
+  int32_t round_bf16; /* GDR_F32 only: nonzero stores the value rounded to bf16 */
+  int32_t reserved;   /* 0 */
+} gdr_linear_out;
+
+/*
+ * y = x W^T, bf16 operands, fp32 accumulation on the matrix cores:
+ *
+ *   x     [M, K] bf16, row stride ldx (elements)
+ *   w     [N, K] bf16, row stride ldw (the out x in layout of a linear layer)
+ *   outs  HOST array of num_outs (1..4) blocks: block i receives output
+ *         columns [c_i, c_i + outs[i].cols) with c_0 = 0, c_{i+1} = c_i +
+ *         outs[i].cols, and N = the sum of the widths
+ *
+ * Each output element is the fp32 sum of the K products, accumulated in an
+ * unspecified order; |y - exact| <= K * 2^-24 * sum_k |x_k w_k| (per element,
+ * before the bf16 rounding of a bf16 or round_bf16 block).
+ * A block whose first column and ld are multiples of 4 and whose pointer is 8-
+ * (bf16) or 16-byte (fp32) aligned is written 4 columns per store; any other
+ * block one element per store.
+ * Errors: INVALID_ARG for M, N < 0, K <= 0, K not a multiple of 128, ldx or
+ * ldw < K or not a multiple of 8, x or w not 16-byte aligned, a bad block
+ * (NULL with M > 0 and cols > 0, cols < 0, ld < cols, bad dtype, pointer not
+ * aligned to its element), widths not summing to N.
+ */
+gdr_status gdr_linear(int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx, const void* w, int64_t ldw,
+                      const gdr_linear_out* outs, int32_t num_outs, void* stream);
+
+/* Shape of the delta layer (gdr_delta_layer_fwd). */
+typedef struct gdr_layer_desc {
+  uint32_t struct_size; /* sizeof(gdr_layer_desc) */
+  int32_t num_tokens;   /* T, packed over all sequences */
+  int32_t num_seqs;     /* N = length of cu_seqlens - 1 */
+  int32_t hidden;       /* H: model width, a multiple of 128 (5120 in the pages' model) */
+  int32_t num_k_heads;  /* Hk */
+  int32_t num_v_heads;  /* Hv, a multiple of Hk */
+  int32_t head_dim;     /* d = d_k = d_v: 128 */
+  float l2norm_eps;     /* q/k L2 norm epsilon (1e-6) */
+  float norm_eps;       /* gated RMS norm epsilon (1e-6) */
+} gdr_layer_desc;
+
+/* Device workspace gdr_delta_layer_fwd needs for *d, in bytes. */
+gdr_status gdr_delta_layer_workspace_size(const gdr_layer_desc* d, size_t* bytes);
+
+/*
+ * Prefill of one whole delta layer over a packed batch:
+ *
+ *   [qkv | z | b | a] = hidden W_in^T        (bf16 results; b, a widened to fp32)
+ *   q, k, v, g, beta  = front(qkv, a, b)      (gdr_conv_gate_fused)
+ *   o, S              = chunk recurrence      (gdr_chunk_fwd: chunk 64, q/k L2
+ *                                              norm in the kernel, scale 1, fp32 o)
+ *   y                 = gated RMS norm(o, z)  (gdr_gated_rmsnorm)
+ *   out               = y W_out^T             (bf16)
+ *
+ * With C = (2*Hk + Hv)*d and V = Hv*d:
+ *   hidden         [T, H] bf16
+ *   w_in           [C + V + 2*Hv, H] bf16: rows for the C conv channels (q | k
+ *                  | v blocks), then the V z channels, then b, then a
+ *   conv_w         [C, 4] bf16;  A_log, dt_bias [Hv] fp32;  norm_w [d] fp32
+ *   w_out          [H, V] bf16
+ *   cu_seqlens     [N+1] int32 device array (required)
+ *   conv_state_in / conv_state_out [N, C, 3] bf16 (NULL = zeros / not written)
+ *   initial_state / final_state    [N, Hv, d, d] fp32 (NULL = zeros / not
+ *                  written; may be the same pointer)
+ *   out            [T, H] bf16
+ *   workspace      >= gdr_delta_layer_workspace_size bytes, 256-byte aligned;
+ *                  holds the intermediates of this call only
+ *
+ * Bit for bit the same as calling gdr_linear, gdr_conv_gate_fused,
+ * gdr_chunk_fwd, gdr_gated_rmsnorm and gdr_linear in turn.  Errors: those of
+ * the five steps; UNSUPPORTED unless d = 128.
+ */
+gdr_status gdr_delta_layer_fwd(const gdr_layer_desc* d, const void* hidden, const void* w_in, const void* conv_w,
+                               const float* A_log, const float* dt_bias, const float* norm_w, const void* w_out,
+                               const int32_t* cu_seqlens, const void* conv_state_in, void* conv_state_out,
+                               const float* initial_state, float* final_state, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -170,6 +170,62 @@ def test_conv_and_norm_validation():
     assert lib.gdr_gated_rmsnorm(None, FAKE, FAKE, FAKE, FAKE, None) == -1
 
 
+def _blocks(*specs):
+    arr = (_lib.GdrLinearOut * len(specs))()
+    for i, (ptr, ld, cols, dt, rnd) in enumerate(specs):
+        arr[i].ptr, arr[i].ld, arr[i].cols, arr[i].dtype, arr[i].round_bf16 = ptr, ld, cols, dt, rnd
+    return arr
+
+
+def test_linear_validation():
+    lib = _lib.load()
+    ok = _blocks((FAKE, 256, 256, 1, 0))
+    assert lib.gdr_linear(4, 256, 192, FAKE, 192, FAKE, 192, ok, 1, None) == -1  # K not a multiple of 128
+    assert "multiple of 128" in lib.gdr_last_error().decode()
+    assert lib.gdr_linear(4, 256, 256, FAKE, 200, FAKE, 256, ok, 1, None) == -1  # ldx not a multiple of 8
+    assert lib.gdr_linear(4, 256, 256, FAKE, 128, FAKE, 256, ok, 1, None) == -1  # ldx < K
+    assert lib.gdr_linear(4, 256, 256, FAKE + 8, 256, FAKE, 256, ok, 1, None) == -1  # x misaligned
+    assert lib.gdr_linear(4, 256, 256, FAKE, 256, FAKE, 256, ok, 0, None) == -1  # no blocks
+    assert lib.gdr_linear(4, 256, 256, FAKE, 256, FAKE, 256, ok, 5, None) == -1  # too many
+    assert lib.gdr_linear(4, 260, 256, FAKE, 256, FAKE, 256, ok, 1, None) == -1  # widths != N
+    assert "sum" in lib.gdr_last_error().decode()
+    assert lib.gdr_linear(4, 8, 256, FAKE, 256, FAKE, 256, _blocks((FAKE + 2, 8, 8, 0, 0)), 1, None) == -1
+    assert lib.gdr_linear(4, 8, 256, FAKE, 256, FAKE, 256, _blocks((FAKE + 1, 8, 8, 1, 0)), 1, None) == -1
+    assert lib.gdr_linear(4, 8, 256, FAKE, 256, FAKE, 256, _blocks((FAKE, 8, -1, 1, 0), (FAKE, 8, 9, 1, 0)),
+                          2, None) == -1
+    assert lib.gdr_linear(4, 8, 256, FAKE, 256, FAKE, 256, _blocks((None, 8, 8, 1, 0)), 1, None) == -1
+    assert lib.gdr_linear(4, 8, 256, FAKE, 256, FAKE, 256, _blocks((FAKE, 4, 8, 1, 0)), 1, None) == -1  # ld<w
+    assert lib.gdr_linear(4, 8, 256, FAKE, 256, FAKE, 256, _blocks((FAKE, 8, 8, 7, 0)), 1, None) == -1  # dtype
+    assert lib.gdr_linear(-1, 8, 256, FAKE, 256, FAKE, 256, ok, 1, None) == -1
+    # nothing to compute: accepted without a launch
+    assert lib.gdr_linear(0, 256, 256, None, 256, None, 256, _blocks((None, 256, 256, 1, 0)), 1, None) == 0
+
+
+def test_delta_layer_validation_and_workspace():
+    lib = _lib.load()
+    d = _lib.GdrLayerDesc()
+    d.struct_size = ctypes.sizeof(_lib.GdrLayerDesc)
+    d.num_tokens, d.num_seqs, d.hidden = 32768, 1, 5120
+    d.num_k_heads, d.num_v_heads, d.head_dim = 16, 48, 128
+    d.l2norm_eps = d.norm_eps = 1e-6
+    n = ctypes.c_size_t(0)
+    assert lib.gdr_delta_layer_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    T, C, V = 32768, 10240, 6144
+    inter = T * (2 * C + 2 * V + 4 * 48 * 4 + 2 * C) + T * V * 4
+    assert inter <= n.value < inter + 700 * 2 ** 20  # plus the recurrence's per-chunk records
+    d.head_dim = 64
+    assert lib.gdr_delta_layer_workspace_size(ctypes.byref(d), ctypes.byref(n)) == -2
+    d.head_dim, d.hidden = 128, 5000
+    assert lib.gdr_delta_layer_workspace_size(ctypes.byref(d), ctypes.byref(n)) == -1
+    d.hidden = 5120
+    args = [FAKE] * 14
+    assert lib.gdr_delta_layer_fwd(ctypes.byref(d), *args, 10, None) == -1  # short workspace
+    assert "workspace" in lib.gdr_last_error().decode()
+    args[7] = None  # no cu_seqlens
+    assert lib.gdr_delta_layer_fwd(ctypes.byref(d), *args, 1 << 40, None) == -1
+    assert lib.gdr_delta_layer_fwd(None, *([FAKE] * 14), 1 << 40, None) == -1
+
+
 def test_no_oracle_in_product_path():
     """The library and its binding never import the oracle."""
     pkg = os.path.join(ROOT, "gated_delta_rule_amd")
