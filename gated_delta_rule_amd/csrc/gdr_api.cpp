@@ -359,7 +359,7 @@ gdr_status gdr_gated_rmsnorm(const gdr_norm_desc* d, const void* o, const void* 
 gdr_status gdr_linear(int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx, const void* w, int64_t ldw,
                       const gdr_linear_out* outs, int32_t num_outs, void* stream) {
   if (M < 0 || N < 0 || K <= 0) return fail(GDR_ERR_INVALID_ARG, "need M, N >= 0 and K > 0 (got %d, %d, %d)", M, N, K);
-  if (K % 128) return fail(GDR_ERR_INVALID_ARG, "K (%d) must be a multiple of 128", K);
+  if (K % 32) return fail(GDR_ERR_INVALID_ARG, "K (%d) must be a multiple of 32", K);
   if (ldx < K || ldw < K || ldx % 8 || ldw % 8)
     return fail(GDR_ERR_INVALID_ARG, "ldx and ldw must be >= K and multiples of 8");
   if (!outs || num_outs < 1 || num_outs > 4) return fail(GDR_ERR_INVALID_ARG, "need 1..4 output blocks");
@@ -434,7 +434,7 @@ gdr_status layer_plan(const gdr_layer_desc* d, LayerBufs* p) {
   if (d->num_v_heads % d->num_k_heads)
     return fail(GDR_ERR_INVALID_ARG, "num_v_heads must be a multiple of num_k_heads");
   if (d->head_dim != 128) return fail(GDR_ERR_UNSUPPORTED, "the delta layer takes head_dim 128 (got %d)", d->head_dim);
-  if (d->hidden % 128) return fail(GDR_ERR_INVALID_ARG, "hidden (%d) must be a multiple of 128", d->hidden);
+  if (d->hidden % 32) return fail(GDR_ERR_INVALID_ARG, "hidden (%d) must be a multiple of 32", d->hidden);
   if (!(d->l2norm_eps >= 0.f) || !(d->norm_eps >= 0.f)) return fail(GDR_ERR_INVALID_ARG, "eps must be >= 0");
   const size_t T = (size_t)d->num_tokens, Hk = d->num_k_heads, Hv = d->num_v_heads, D = d->head_dim;
   const size_t C = (2 * Hk + Hv) * D, V = Hv * D;

@@ -87,7 +87,7 @@ struct LinearArgs {
   const void* x;  // [M, K] bf16, row stride ldx
   const void* w;  // [N, K] bf16, row stride ldw
   int64_t ldx, ldw;
-  int M, N, K;    // K a multiple of 128
+  int M, N, K;    // K a multiple of 32
   int nout;       // 1..4 blocks, contiguous, out[0].n0 = 0, empty ones allowed
   LinearOut out[4];
 };

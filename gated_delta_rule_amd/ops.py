@@ -317,7 +317,7 @@ def gated_rmsnorm(o: torch.Tensor, z: torch.Tensor, w: torch.Tensor, eps: float 
 def linear(x: torch.Tensor, w: torch.Tensor, blocks=None, out_dtype: torch.dtype = torch.bfloat16):
     """Dense projection y = x W^T (gdr_linear): bf16 operands, fp32 accumulation.
 
-    x: [M, K] bf16, w: [N, K] bf16 (K a multiple of 128).  Without ``blocks``
+    x: [M, K] bf16, w: [N, K] bf16 (K a multiple of 32).  Without ``blocks``
     returns one [M, N] tensor of ``out_dtype`` (bf16 or fp32).  ``blocks`` is a
     list of (width, dtype) or (width, dtype, round_bf16) splitting the N output
     columns into separate tensors, returned as a list.

@@ -322,7 +322,7 @@ typedef struct gdr_linear_out {
  * A block whose first column and ld are multiples of 4 and whose pointer is 8-
  * (bf16) or 16-byte (fp32) aligned is written 4 columns per store; any other
  * block one element per store.
- * Errors: INVALID_ARG for M, N < 0, K <= 0, K not a multiple of 128, ldx or
+ * Errors: INVALID_ARG for M, N < 0, K <= 0, K not a multiple of 32, ldx or
  * ldw < K or not a multiple of 8, x or w not 16-byte aligned, a bad block
  * (NULL with M > 0 and cols > 0, cols < 0, ld < cols, bad dtype, pointer not
  * aligned to its element), widths not summing to N.
@@ -335,7 +335,7 @@ typedef struct gdr_layer_desc {
   uint32_t struct_size; /* sizeof(gdr_layer_desc) */
   int32_t num_tokens;   /* T, packed over all sequences */
   int32_t num_seqs;     /* N = length of cu_seqlens - 1 */
-  int32_t hidden;       /* H: model width, a multiple of 128 (5120 in the pages' model) */
+  int32_t hidden;       /* H: model width, a multiple of 32 (5120 in the pages' model) */
   int32_t num_k_heads;  /* Hk */
   int32_t num_v_heads;  /* Hv, a multiple of Hk */
   int32_t head_dim;     /* d = d_k = d_v: 128 */

@@ -180,8 +180,8 @@ def _blocks(*specs):
 def test_linear_validation():
     lib = _lib.load()
     ok = _blocks((FAKE, 256, 256, 1, 0))
-    assert lib.gdr_linear(4, 256, 192, FAKE, 192, FAKE, 192, ok, 1, None) == -1  # K not a multiple of 128
-    assert "multiple of 128" in lib.gdr_last_error().decode()
+    assert lib.gdr_linear(4, 256, 200, FAKE, 200, FAKE, 200, ok, 1, None) == -1  # K not a multiple of 32
+    assert "multiple of 32" in lib.gdr_last_error().decode()
     assert lib.gdr_linear(4, 256, 256, FAKE, 200, FAKE, 256, ok, 1, None) == -1  # ldx not a multiple of 8
     assert lib.gdr_linear(4, 256, 256, FAKE, 128, FAKE, 256, ok, 1, None) == -1  # ldx < K
     assert lib.gdr_linear(4, 256, 256, FAKE + 8, 256, FAKE, 256, ok, 1, None) == -1  # x misaligned
