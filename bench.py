@@ -16,6 +16,9 @@ in the same run:
                gated RMS norm), beside the same work as three launches
   pipeline  -- the whole layer path over a packed batch of 8 sequences
                (65536 tokens): conv+SiLU+gates, recurrence, gated RMSNorm
+  layer     -- one whole delta layer on a 32768-token sequence with synthetic
+               weights: in-projection GEMM, the path, out-projection GEMM
+               (hidden 5120); stage times and the GEMMs' matrix-core rate
   roofline  -- the dominant kernel of the call, the state-carrying
                recurrence (gdr_chunk_fwd_recurrence): its algorithmic HBM bytes
                per launch (q, k, v read, o written, state in and out) over its
@@ -32,7 +35,7 @@ in the same run:
                and 4 decode steps for the decode leg)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pieces P] [--no-cpu]
-                       [--only prefill|decode|decode_layer|pipeline|copy|roofline|all]
+                       [--only prefill|decode|decode_layer|pipeline|layer|copy|roofline|all]
 """
 from __future__ import annotations
 
@@ -337,6 +340,98 @@ def bench_pipeline(reps: int = 5):
                 recurrence_tokens_per_s=T / (med["recurrence"] * 1e-3))
 
 
+def bench_layer(reps: int = 5):
+    """One whole delta layer's prefill on a 32768-token sequence with synthetic
+    weights (hidden 5120): in-projection GEMM (5120 -> q|k|v 10240, z 6144,
+    b 48, a 48), conv front, chunked recurrence, gated RMS norm, out-projection
+    GEMM (6144 -> 5120), as gdr_delta_layer_fwd.  Stage times come from the
+    same five steps called one by one (HIP events on the launch stream).  The
+    projections' rate is set against the bf16 matrix-core peak; torch.matmul
+    on the same operands (hipBLASLt) is timed beside them as a reference."""
+    import torch
+    import gated_delta_rule_amd as gdr
+    from gated_delta_rule_amd import synth
+    dev = torch.device("cuda:0")
+    T, H = T_CALL, synth.HIDDEN
+    Cq, V = (2 * HK + HV) * D, HV * D
+    log(f"layer: T={T}, hidden={H}, generating synthetic weights")
+    L = synth.layer_inputs(6, lengths=(T,))
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).to(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    hid, w_in, w_out, cw = bf(L.hidden), bf(L.w_in), bf(L.w_out), bf(L.conv_w)
+    Al, dtb, nw = f32(L.A_log), f32(L.dt_bias), f32(L.norm_w)
+    cu = torch.from_numpy(L.cu_seqlens.astype(np.int32)).to(dev)
+    del L
+    st = torch.zeros((1, HV, D, D), device=dev)
+    out = torch.empty((T, H), device=dev, dtype=torch.bfloat16)
+    ws = gdr.delta_layer_workspace(T, 1, H, HK, HV, D, device=dev)
+    chunk_ws = gdr.chunk_workspace(torch.empty((1, T, HK, D), device=dev, dtype=torch.bfloat16),
+                                   torch.empty((1, T, HV, D), device=dev, dtype=torch.bfloat16), cu)
+
+    def layer():
+        gdr.delta_layer_fwd(hid, w_in, cw, Al, dtb, nw, w_out, cu, HK, HV, D, initial_state=st,
+                            final_state=st, out=out, workspace=ws)
+
+    for _ in range(2):
+        layer()
+    torch.cuda.synchronize()
+    start, end = _events()
+    start.record()
+    for _ in range(reps):
+        layer()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+
+    names = ("in_proj", "front", "recurrence", "norm", "out_proj")
+    acc = {n: 0.0 for n in names}
+    for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record()
+        qkv, z, b, a = gdr.linear(hid, w_in, blocks=[(Cq, torch.bfloat16), (V, torch.bfloat16),
+                                                     (HV, torch.float32, True), (HV, torch.float32, True)])
+        ev[1].record()
+        q, k, v, g, beta, _ = gdr.conv_gate_fused(qkv, cw, cu, a, b, Al, dtb, HK, HV, D)
+        ev[2].record()
+        o, _ = gdr.chunk_gated_delta_rule(q, k, v, g, beta, st, cu_seqlens=cu, final_state=st, workspace=chunk_ws)
+        ev[3].record()
+        y = gdr.gated_rmsnorm(o[0], z, nw)
+        ev[4].record()
+        gdr.linear(y, w_out)
+        ev[5].record()
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1]) / reps
+        del qkv, z, b, a, q, k, v, g, beta, o, y
+
+    def mm_ms(x, w):
+        wt = w.t()
+        for _ in range(2):
+            torch.matmul(x, wt)
+        torch.cuda.synchronize()
+        s0, s1 = _events()
+        s0.record()
+        for _ in range(reps):
+            torch.matmul(x, wt)
+        s1.record()
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / reps
+
+    ref_in = mm_ms(hid, w_in)
+    y = torch.empty((T, V), device=dev, dtype=torch.bfloat16).normal_()
+    ref_out = mm_ms(y, w_out)
+    f_in = 2.0 * T * (Cq + V + 2 * HV) * H
+    f_out = 2.0 * T * V * H
+    tf = lambda f, t: f / (t * 1e-3) / 1e12
+    gemm_tf = tf(f_in + f_out, acc["in_proj"] + acc["out_proj"])
+    return dict(tokens_per_s=T / (ms * 1e-3), ms=ms, stages_ms=acc,
+                gemm={"in_proj_TFLOPs": tf(f_in, acc["in_proj"]), "out_proj_TFLOPs": tf(f_out, acc["out_proj"]),
+                      "TFLOPs": gemm_tf, "frac_bf16_peak": gemm_tf / BF16_PEAK_TFLOPS,
+                      "hipblaslt_in_proj_TFLOPs": tf(f_in, ref_in), "hipblaslt_out_proj_TFLOPs": tf(f_out, ref_out)},
+                config={"T": T, "hidden": H, "num_k_heads": HK, "num_v_heads": HV, "head_dim": D,
+                        "weights": "synthetic, N(0, 1/fan_in)"})
+
+
 def bench_copy(n_bytes: int = 1 << 30, reps: int = 5):
     """Plain device copy of known size: calibration of the HBM byte counters."""
     import torch
@@ -423,8 +518,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=24)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "decode_layer", "pipeline", "copy",
-                                                      "roofline"])
+    ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "decode_layer", "pipeline", "layer",
+                                                      "copy", "roofline"])
     ap.add_argument("--pieces", type=int, default=N_CALLS,
                     help="distinct 32K pieces of the context to cycle through (8 = the whole 262144 tokens)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -502,6 +597,8 @@ def main():
         out["decode_layer"] = bench_decode_layer()
     if args.only in ("all", "pipeline"):
         out["pipeline"] = bench_pipeline()
+    if args.only in ("all", "layer"):
+        out["layer"] = bench_layer()
     if args.only == "all":
         ach = bench_roofline()
         out["achievable"] = ach
