@@ -184,3 +184,45 @@ def test_layer_small_against_oracle(lengths, hidden, hk, hv):
     e2e = rel_err(to_host(out), r["out"])
     say(f"  end-to-end max err / RMS = {e2e:.3e}")
     assert e2e <= 5e-2
+
+
+def test_layer_full_size_sampled():
+    """The layer at the benchmark's size: one 32768-token sequence, hidden
+    5120, 16/48 heads.  Equal bit for bit to its five steps; the projections
+    checked on sampled rows, the front on sampled channels (bit-exact), the
+    recurrence on two value heads over the first 2048 tokens, the norm and
+    the output projection on sampled rows, each against the oracle fed that
+    step's GPU inputs."""
+    import torch
+    dev = gpu()
+    T, hk, hv, d = 32768, 16, 48, 128
+    L = synth.layer_inputs(6, lengths=(T,))
+    C, V = (2 * hk + hv) * d, hv * d
+    say("delta layer full size T=32768 hidden=5120")
+    w, out, fin, cso = _layer_gpu(L, dev)
+    torch.cuda.synchronize()
+    s = _stages(L, w, dev)
+    assert bits_equal(out, s["out"]) and bits_equal(fin, s["final_state"])
+    rng = synth.rng(77)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, T - 1], rng.choice(T, 27, replace=False)]))
+    rd = torch.as_tensor(rows, device=dev)
+    # in-projection on sampled rows, every column
+    proj = np.concatenate([to_host(s[n][rd]) for n in ("qkv", "z", "b", "a")], 1)
+    _check(proj, lref.linear(L.hidden[rows], L.w_in), _bound(L.hidden[rows], L.w_in), True)
+    # front on sampled channels, every token
+    cols = np.unique(np.concatenate([np.arange(0, 16), np.arange(2040, 2056), np.arange(C - 16, C),
+                                     rng.choice(C, 48, replace=False)]))
+    qkv_c = to_host(s["qkv"][:, torch.as_tensor(cols, device=dev)]).astype(np.float32)
+    gq = torch.cat([s[n].reshape(T, -1) for n in ("q", "k", "v")], 1)[:, torch.as_tensor(cols, device=dev)]
+    assert np.array_equal(to_host(gq), cref.conv_silu_fp32(qkv_c, L.conv_w[cols], L.cu_seqlens))
+    # recurrence: two value heads, first 2048 tokens
+    heads = [0, 47]
+    qh, kh, vh, gh, bh = (to_host(s[n]).astype(np.float32) for n in ("q", "k", "v", "g", "beta"))
+    o_ref, _ = gref.forward(qh, kh, vh, gh, bh, None, L.cu_seqlens, heads=heads, token_limit=2048)
+    og = to_host(s["o"])
+    assert rel_err(og[:, :2048][:, :, heads], o_ref[:, :2048][:, :, heads]) <= BF16_TOL
+    # norm and out-projection on sampled rows
+    y_ref = cref.gated_rmsnorm(og[0][rows], to_host(s["z"][rd]).reshape(len(rows), hv, d), L.norm_w)
+    assert np.all(np.abs(to_host(s["y"][rd]) - y_ref.reshape(len(rows), V)) <= bf16_ulp(y_ref.reshape(len(rows), V)) + 1e-30)
+    yh = to_host(s["y"][rd]).astype(np.float32)
+    _check(to_host(out[rd]), lref.linear(yh, L.w_out), _bound(yh, L.w_out), True)
