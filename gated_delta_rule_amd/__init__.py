@@ -6,6 +6,8 @@ if it has not been built (``python -m gated_delta_rule_amd.build``).
 """
 from ._lib import GDRError, load as load_library  # noqa: F401
 from .ops import (  # noqa: F401
+    attn_prefill,
+    attn_qk_norm_rope,
     chunk_gated_delta_rule,
     chunk_workspace,
     conv_gate_fused,
@@ -29,4 +31,6 @@ __all__ = [
     "linear",
     "delta_layer_fwd",
     "delta_layer_workspace",
+    "attn_prefill",
+    "attn_qk_norm_rope",
 ]

@@ -30,6 +30,9 @@ EXPORTED = (
     "gdr_linear",
     "gdr_delta_layer_workspace_size",
     "gdr_delta_layer_fwd",
+    "gdr_attn_qk_norm_rope",
+    "gdr_attn_prefill_workspace_size",
+    "gdr_attn_prefill",
 )
 
 
@@ -99,6 +102,20 @@ class GdrLayerDesc(ctypes.Structure):
     ]
 
 
+class GdrAttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("num_tokens", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("cache_len", ctypes.c_int32),
+        ("norm_eps", ctypes.c_float),
+        ("rope_base", ctypes.c_double),
+    ]
+
+
 class GDRError(RuntimeError):
     """A libgdr entry point returned a negative status."""
 
@@ -152,6 +169,12 @@ def load() -> ctypes.CDLL:
     lib.gdr_delta_layer_workspace_size.argtypes = [ctypes.POINTER(GdrLayerDesc), ctypes.POINTER(SZ)]
     lib.gdr_delta_layer_fwd.restype = I32
     lib.gdr_delta_layer_fwd.argtypes = [ctypes.POINTER(GdrLayerDesc)] + [P] * 14 + [SZ, P]
+    lib.gdr_attn_qk_norm_rope.restype = I32
+    lib.gdr_attn_qk_norm_rope.argtypes = [ctypes.POINTER(GdrAttnDesc)] + [P] * 8
+    lib.gdr_attn_prefill_workspace_size.restype = I32
+    lib.gdr_attn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdrAttnDesc), ctypes.POINTER(SZ)]
+    lib.gdr_attn_prefill.restype = I32
+    lib.gdr_attn_prefill.argtypes = [ctypes.POINTER(GdrAttnDesc)] + [P] * 11 + [SZ, P]
     _lib = lib
     return lib
 

@@ -31,6 +31,7 @@ SOURCES = [
     "kernels/conv_front.hip",
     "kernels/gated_rmsnorm.hip",
     "kernels/linear_bf16.hip",
+    "kernels/attention.hip",
 ]
 ROOFLINE_SOURCES = ["roofline/roofline.hip"]
 
@@ -55,9 +56,9 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libgdr)")
 
 
-# The GEMM keeps its 256 accumulators per lane in the accumulation
-# registers, so it is built without the VGPR form.
-NO_VGPR_FORM = {"kernels/linear_bf16.hip"}
+# The GEMM and the attention kernel keep their accumulators in the
+# accumulation registers, so they are built without the VGPR form.
+NO_VGPR_FORM = {"kernels/linear_bf16.hip", "kernels/attention.hip"}
 
 
 def _compile(src: str, verbose: bool) -> str:

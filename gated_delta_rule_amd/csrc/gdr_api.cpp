@@ -536,4 +536,93 @@ gdr_status gdr_delta_layer_fwd(const gdr_layer_desc* d, const void* hidden, cons
   return gdr_linear(T, H, V, y, V, w_out, V, &out_blk, 1, stream);
 }
 
+namespace {
+
+gdr_status check_attn(const gdr_attn_desc* d, bool decode) {
+  if (!d) return fail(GDR_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->struct_size < sizeof(gdr_attn_desc))
+    return fail(GDR_ERR_INVALID_ARG, "descriptor struct_size %u < %zu", d->struct_size, sizeof(gdr_attn_desc));
+  if (d->num_tokens < 0 || d->num_seqs < 1 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->cache_len < 0)
+    return fail(GDR_ERR_INVALID_ARG, "need num_tokens >= 0, num_seqs >= 1, positive heads, cache_len >= 0");
+  if (d->head_dim != 256) return fail(GDR_ERR_UNSUPPORTED, "attention takes head_dim 256 (got %d)", d->head_dim);
+  if (d->num_q_heads % d->num_kv_heads)
+    return fail(GDR_ERR_UNSUPPORTED, "num_q_heads must be a multiple of num_kv_heads");
+  if (!(d->norm_eps >= 0.f) || !(d->rope_base > 1.0)) return fail(GDR_ERR_INVALID_ARG, "need eps >= 0, rope_base > 1");
+  if (decode && d->num_tokens != d->num_seqs) return fail(GDR_ERR_INVALID_ARG, "decode needs num_tokens == num_seqs");
+  return ok();
+}
+
+gdr::AttnArgs attn_args(const gdr_attn_desc* d) {
+  gdr::AttnArgs a{};
+  a.T = d->num_tokens;
+  a.N = d->num_seqs;
+  a.Hq = d->num_q_heads;
+  a.Hk = d->num_kv_heads;
+  a.cache_len = d->cache_len;
+  a.eps = d->norm_eps;
+  a.rope_base = d->rope_base;
+  return a;
+}
+
+}  // namespace
+
+gdr_status gdr_attn_qk_norm_rope(const gdr_attn_desc* d, const void* q, const void* k, const float* q_norm_w,
+                                 const float* k_norm_w, const int32_t* cu_seqlens, void* q_out, void* k_out,
+                                 void* stream) {
+  gdr_status st = check_attn(d, false);
+  if (st != GDR_OK) return st;
+  if (!cu_seqlens || !q_norm_w || !k_norm_w) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens and the norm weights are required");
+  if (d->num_tokens > 0 && (!q || !k || !q_out || !k_out)) return fail(GDR_ERR_INVALID_ARG, "q, k, q_out and k_out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(q_norm_w) ||
+      !aligned16(k_norm_w))
+    return fail(GDR_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  gdr::AttnArgs a = attn_args(d);
+  a.q = q;
+  a.k = k;
+  a.q_norm_w = q_norm_w;
+  a.k_norm_w = k_norm_w;
+  a.cu_seqlens = cu_seqlens;
+  return hip_status(gdr::launch_attn_qk_prep(a, q_out, k_out, static_cast<hipStream_t>(stream)),
+                    "gdr_attn_qk_norm_rope launch");
+}
+
+gdr_status gdr_attn_prefill_workspace_size(const gdr_attn_desc* d, size_t* bytes) {
+  if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+  const gdr_status st = check_attn(d, false);
+  if (st != GDR_OK) return st;
+  *bytes = gdr::attn_prefill_workspace_bytes(attn_args(d));
+  return ok();
+}
+
+gdr_status gdr_attn_prefill(const gdr_attn_desc* d, const void* q, const void* k, const void* v, const void* gate,
+                            const float* q_norm_w, const float* k_norm_w, const int32_t* cu_seqlens, void* out,
+                            void* k_cache, void* v_cache, void* workspace, size_t workspace_bytes, void* stream) {
+  gdr_status st = check_attn(d, false);
+  if (st != GDR_OK) return st;
+  if (!cu_seqlens || !q_norm_w || !k_norm_w) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens and the norm weights are required");
+  if (d->num_tokens > 0 && (!q || !k || !v || !gate || !out))
+    return fail(GDR_ERR_INVALID_ARG, "q, k, v, gate and out are required");
+  if (!k_cache != !v_cache) return fail(GDR_ERR_INVALID_ARG, "give both k_cache and v_cache or neither");
+  if (k_cache && d->cache_len <= 0) return fail(GDR_ERR_INVALID_ARG, "a cache needs cache_len > 0");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(out) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(q_norm_w) || !aligned16(k_norm_w))
+    return fail(GDR_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  gdr::AttnArgs a = attn_args(d);
+  const size_t need = gdr::attn_prefill_workspace_bytes(a);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDR_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace ? workspace_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GDR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gate = gate;
+  a.q_norm_w = q_norm_w;
+  a.k_norm_w = k_norm_w;
+  a.cu_seqlens = cu_seqlens;
+  a.out = out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  return hip_status(gdr::launch_attn_prefill(a, workspace, static_cast<hipStream_t>(stream)), "gdr_attn_prefill launch");
+}
+
 }  // extern "C"

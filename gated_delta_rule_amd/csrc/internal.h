@@ -92,8 +92,26 @@ struct LinearArgs {
   LinearOut out[4];
 };
 
+// Global attention (GQA, head dim 256): prefill over a packed batch, and one
+// decode token per sequence against a KV cache.
+struct AttnArgs {
+  const void *q, *k, *v, *gate;    // bf16: q, gate [rows, Hq, 256]; k, v [rows, Hk, 256]
+  const float *q_norm_w, *k_norm_w;  // [256]
+  const int32_t* cu_seqlens;       // prefill [N+1]
+  const int32_t* cache_lens;       // decode [N]: cached tokens before this one
+  void* out;                       // [rows, Hq, 256] bf16
+  void *k_cache, *v_cache;         // [N, cache_len, Hk, 256] bf16 or NULL (prefill)
+  int cache_len;
+  int T, N, Hq, Hk;                // T: packed tokens (prefill) or N (decode)
+  float eps;
+  double rope_base;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_linear(const LinearArgs& a, hipStream_t st);
+size_t attn_prefill_workspace_bytes(const AttnArgs& a);
+hipError_t launch_attn_qk_prep(const AttnArgs& a, void* q_out, void* k_out, hipStream_t st);
+hipError_t launch_attn_prefill(const AttnArgs& a, void* workspace, hipStream_t st);
 hipError_t launch_decode_layer(const LayerStepArgs& a, hipStream_t st);
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t st);
 // The bf16-MFMA prefill needs a device workspace of

@@ -1,0 +1,509 @@
+// The global attention layer of the hybrid decoder: grouped-query attention
+// with an RMS norm on q and k, rotary encoding on the first 64 dims of each
+// head and a sigmoid gate on the output (deepmagic page, architecture
+// section: 24 query / 4 key-value heads, head dim 256, q/k RMS norm, sigmoid
+// output gate, rotary encoding on the first quarter of each head with base
+// 1e7; kongchang page, attention details).
+//
+// Prefill, three launches:
+//   attn_table_kernel  per-sequence offsets of 64-key chunks and 128-query
+//                      blocks (prefix sums over cu_seqlens)
+//   attn_prep_kernel   per token: RMS norm of every q and k head, rotation
+//                      of dims (j, j + 32), j < 32; q to a bf16 buffer, k to a
+//                      key buffer padded per sequence to whole 64-key chunks
+//                      (and to the caller's KV cache)
+//   attn_vt_kernel     V transposed per 64-key chunk (dims x keys), so both
+//                      products below read 16 contiguous bytes per lane
+//   attn_fwd_kernel    causal attention, one workgroup per (query head,
+//                      128-query block), 64-key blocks through LDS
+// Decode: attn_prep_kernel (one row per sequence, at its cache position,
+// appending k and v to the cache), attn_decode_kernel (split over the cached
+// keys) and attn_combine_kernel (merges the splits, applies the gate).
+#include "../common.h"
+#include "../internal.h"
+
+namespace gdr {
+
+namespace {
+
+constexpr int kAD = 256;      // head dim
+constexpr int kRot = 64;      // rotated dims
+constexpr int kQB = 128;      // queries per workgroup (4 waves x 32)
+constexpr int kKB = 64;       // keys per block
+constexpr int kXcds = 8;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// One 16-byte direct-to-LDS load per lane: lane l's bytes land at LDS byte
+// address lds_addr + 16 l.  No register receives data; waits are explicit.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Index of the sequence holding item i, given offsets off[0..N] (off[0] = 0,
+// non-decreasing): the largest n < N with off[n] <= i.
+__device__ __forceinline__ int find_seq(const int32_t* off, int N, int i) {
+  int lo = 0, hi = N - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= i)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// Per-sequence offsets: table[n] = sum over m < n of ceil(L_m / 64) (key
+// chunks), table[N + 1 + n] = sum of ceil(L_m / 128) (query blocks), n = 0..N.
+__global__ __launch_bounds__(256) void attn_table_kernel(const int32_t* cu, int N, int32_t* table) {
+  __shared__ int32_t s_c[256], s_q[256];
+  const int tid = threadIdx.x;
+  const int per = (N + 255) / 256, a = tid * per, b = min(a + per, N);
+  int c = 0, q = 0;
+  for (int n = a; n < b; ++n) {
+    const int L = cu[n + 1] - cu[n];
+    c += (L + kKB - 1) / kKB;
+    q += (L + kQB - 1) / kQB;
+  }
+  s_c[tid] = c;
+  s_q[tid] = q;
+  __syncthreads();
+  if (tid == 0) {
+    int rc = 0, rq = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int tc = s_c[i], tq = s_q[i];
+      s_c[i] = rc;
+      s_q[i] = rq;
+      rc += tc;
+      rq += tq;
+    }
+    table[N] = rc;
+    table[N + 1 + N] = rq;
+  }
+  __syncthreads();
+  c = s_c[tid];
+  q = s_q[tid];
+  for (int n = a; n < b; ++n) {
+    table[n] = c;
+    table[N + 1 + n] = q;
+    const int L = cu[n + 1] - cu[n];
+    c += (L + kKB - 1) / kKB;
+    q += (L + kQB - 1) / kQB;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RMS norm + rotation of one token's heads.  One workgroup per token (prefill)
+// or per sequence (decode, one new token at its cache position).  Waves take
+// heads round-robin; lane l holds dims 4l .. 4l+3.
+struct PrepArgs {
+  const uint16_t *q, *k, *v;     // [rows, Hq | Hk, D] bf16
+  const float *q_w, *k_w;        // [D]
+  const int32_t* cu;             // prefill: cu_seqlens [N+1]; decode: NULL
+  const int32_t* table;          // prefill: key-chunk offsets [N+1]
+  const int32_t* cache_lens;     // decode: [N] position of the new token
+  uint16_t* q_rot;               // [rows, Hq, D]
+  uint16_t* k_pad;               // prefill: [64 * chunks, Hk, D] or NULL
+  uint16_t* k_rot;               // [rows, Hk, D] or NULL (the rotated k, unpadded)
+  uint16_t *k_cache, *v_cache;   // [N, cache_len, Hk, D] or NULL
+  int rows, N, Hq, Hk, cache_len;
+  float eps;
+  double base;
+};
+
+__global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
+  __shared__ float s_cos[kRot / 2], s_sin[kRot / 2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = blockIdx.x;
+  int n, pos;
+  if (a.cu) {
+    n = find_seq(a.cu, a.N, t);
+    pos = t - a.cu[n];
+  } else {
+    n = t;
+    pos = a.cache_lens[t];
+  }
+  if (tid < kRot / 2) {
+    // angle pos * base^(-2j/64) in fp64, reduced to [-pi, pi] before the
+    // fp32 sine and cosine, so large positions keep their accuracy
+    const double inv = pow(a.base, -2.0 * tid / kRot);
+    const double ang = (double)pos * inv;
+    const double two_pi = 6.283185307179586476925287;
+    const float r = (float)(ang - two_pi * rint(ang / two_pi));
+    s_cos[tid] = cosf(r);
+    s_sin[tid] = sinf(r);
+  }
+  __syncthreads();
+  const bool to_cache = a.k_cache && pos < a.cache_len;
+  for (int hh = wave; hh < a.Hq + a.Hk; hh += 4) {
+    const bool is_q = hh < a.Hq;
+    const int h = is_q ? hh : hh - a.Hq;
+    const uint16_t* src = is_q ? a.q + ((size_t)t * a.Hq + h) * kAD : a.k + ((size_t)t * a.Hk + h) * kAD;
+    const u16x4 raw = *reinterpret_cast<const u16x4*>(src + 4 * lane);
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = bf16_to_f32(raw[e]);
+    float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+    ss = group_sum<64>(ss);
+    const float rn = 1.f / sqrtf(ss / kAD + a.eps);
+    const float* w = is_q ? a.q_w : a.k_w;
+    const f32x4 wv = *reinterpret_cast<const f32x4*>(w + 4 * lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = x[e] * rn * wv[e];
+    // rotation: lanes 0..7 hold dims 0..31 (first of each pair), lanes
+    // 8..15 dims 32..63 (second); partner lane l ^ 8
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float o = __shfl_xor(x[e], 8, 64);
+      y[e] = x[e];
+      if (lane < 8) {
+        const int j = 4 * lane + e;
+        y[e] = x[e] * s_cos[j] - o * s_sin[j];
+      } else if (lane < 16) {
+        const int j = 4 * (lane - 8) + e;
+        y[e] = x[e] * s_cos[j] + o * s_sin[j];
+      }
+    }
+    const u32x2 out = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    if (is_q) {
+      *reinterpret_cast<u32x2*>(a.q_rot + ((size_t)t * a.Hq + h) * kAD + 4 * lane) = out;
+    } else {
+      if (a.k_pad) {
+        const size_t tp = (size_t)kKB * a.table[n] + pos;
+        *reinterpret_cast<u32x2*>(a.k_pad + (tp * a.Hk + h) * kAD + 4 * lane) = out;
+      }
+      if (a.k_rot) *reinterpret_cast<u32x2*>(a.k_rot + ((size_t)t * a.Hk + h) * kAD + 4 * lane) = out;
+      if (to_cache) {
+        const size_t c = ((size_t)n * a.cache_len + pos) * a.Hk + h;
+        *reinterpret_cast<u32x2*>(a.k_cache + c * kAD + 4 * lane) = out;
+        *reinterpret_cast<u16x4*>(a.v_cache + c * kAD + 4 * lane) =
+            *reinterpret_cast<const u16x4*>(a.v + ((size_t)t * a.Hk + h) * kAD + 4 * lane);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// V transposed per 64-key chunk: vt[h][d][64 c + slot] with keys in slot
+// order kPerm (within each group of 16 keys the middle two quarters swap),
+// the order in which the attention kernel's probabilities come out of its
+// score registers.  Keys past the sequence end are zero.
+__device__ __forceinline__ int kperm(int i) {
+  const int q = (i >> 2) & 3;
+  return (i & ~12) | ((q == 1 ? 2 : q == 2 ? 1 : q) << 2);
+}
+
+__global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* v, const int32_t* cu, const int32_t* table,
+                                                      int N, int Hk, int64_t tpad, uint16_t* vt) {
+  __shared__ uint16_t tile[kKB][kAD + 2];
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  if (c >= table[N]) return;
+  const int n = find_seq(table, N, c);
+  const int L = cu[n + 1] - cu[n], k0 = kKB * (c - table[n]);
+  for (int i = tid; i < kKB * kAD / 4; i += 256) {
+    const int key = i / (kAD / 4), d4 = i % (kAD / 4);
+    u16x4 val = {0, 0, 0, 0};
+    if (k0 + key < L) val = *reinterpret_cast<const u16x4*>(v + ((size_t)(cu[n] + k0 + key) * Hk + h) * kAD + 4 * d4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[key][4 * d4 + e] = val[e];
+  }
+  __syncthreads();
+  const int d = tid;  // one dim (row of vt) per thread: 64 keys, 128 bytes
+  uint16_t row[kKB];
+#pragma unroll
+  for (int s = 0; s < kKB; ++s) row[s] = tile[(s & ~15) | kperm(s & 15)][d];
+  uint16_t* dst = vt + ((size_t)h * kAD + d) * tpad + (size_t)kKB * c;
+#pragma unroll
+  for (int s = 0; s < kKB; s += 8) {
+    u16x8 pk;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pk[e] = row[s + e];
+    *reinterpret_cast<u16x8*>(dst + s) = pk;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Causal attention.  Workgroup: one query head, 128 queries of one sequence,
+// 4 waves of 32 queries.  Per 64-key block, staged in LDS (two stages of a
+// K tile [64 keys][256] and a V^T tile [256 dims][64 keys]):
+//   S^T = K Q^T   16 x 2 MFMAs (32x32x16): lane l holds query l % 32 and 16
+//                 of the block's keys per 32-key tile, so its softmax row
+//                 is in registers (the other 32 keys are in lane l ^ 32)
+//   online softmax in base 2 with a running maximum per query; the
+//                 accumulator is rescaled only when the maximum grows by more
+//                 than 8 (probabilities stay below 2^8)
+//   O^T += V^T P^T  8 dim tiles x 4 key steps: P comes straight from the
+//                 score registers (bf16), V^T from LDS
+// LDS swizzles put the 16 lanes of one 16-byte read on 16 bank groups:
+// K rows (512 B) use chunk c ^ (row & 15), V^T rows (128 B) c ^ ((row >> 1) & 7).
+struct FwdArgs {
+  const uint16_t *q_rot, *k_pad, *vt, *gate;
+  const int32_t *cu, *table;
+  uint16_t* out;
+  int N, Hq, Hk;
+  int64_t tpad;
+  float scale_log2;  // log2(e) / sqrt(D)
+};
+
+constexpr float kRescale = 8.f;
+
+__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* s, int row, int pitch_chunks, int chunk) {
+  return *reinterpret_cast<const bf16x8*>(s + row * pitch_chunks * 8 + 8 * chunk);
+}
+
+__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
+  __shared__ __align__(16) uint16_t sK[2][kKB * kAD], sV[2][kAD * kKB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = a.Hq / a.Hk;
+  // workgroup -> (kv head, query block, member head); the G query heads of
+  // one kv head and block run on one XCD; heaviest blocks (latest in their
+  // sequence) first
+  const int nqb = a.table[a.N + 1 + a.N];
+  const int units = nqb * a.Hk;
+  const int x = blockIdx.x % kXcds, loc = blockIdx.x / kXcds;
+  const int u = (loc / G) * kXcds + x, m = loc % G;
+  if (u >= units) return;
+  const int kvh = u % a.Hk, qb = nqb - 1 - u / a.Hk;
+  const int h = kvh * G + m;
+  const int32_t* qoff = a.table + a.N + 1;
+  const int n = find_seq(qoff, a.N, qb);
+  const int s0 = a.cu[n], L = a.cu[n + 1] - s0;
+  const int q0 = kQB * (qb - qoff[n]);                 // first query of the block (in the sequence)
+  const int qw = q0 + 32 * wave;                       // first query of this wave
+  const int my_q = min(qw + (lane & 31), L - 1);       // this lane's query (rows past L repeat the last)
+  const int last_q = min(q0 + kQB - 1, L - 1);
+  const int nkb = last_q / kKB + 1;
+  const int64_t kp0 = (int64_t)kKB * a.table[n];       // first padded key of the sequence
+
+  // Q^T fragments (B operand): query my_q, dims 16 ks + 8 (l / 32) .. +7
+  bf16x8 qf[16];
+  {
+    const uint16_t* qrow = a.q_rot + ((size_t)(s0 + my_q) * a.Hq + h) * kAD + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+  }
+
+  f32x16 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+  float mrun = -INFINITY, lsum = 0.f;
+
+  // copy of key block j into stage st: this wave's 8 K pieces (2 rows each)
+  // and 8 V^T pieces (8 rows each)
+  auto copy_piece = [&](int j, int st, int i) {
+    if (i < 8) {
+      const int row = 16 * wave + 2 * i + (lane >> 5);
+      const int c = (lane & 31) ^ (row & 15);
+      const uint16_t* g = a.k_pad + ((kp0 + (int64_t)kKB * j + row) * a.Hk + kvh) * kAD + 8 * c;
+      dma16(g, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)(sK[st] + (16 * wave + 2 * i) * kAD)));
+    } else {
+      const int r0 = 64 * wave + 8 * (i - 8), row = r0 + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
+      const uint16_t* g = a.vt + ((int64_t)kvh * kAD + row) * a.tpad + kp0 + (int64_t)kKB * j + 8 * c;
+      dma16(g, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)(sV[st] + r0 * kKB)));
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < 16; ++i) copy_piece(0, 0, i);
+
+  for (int j = 0; j < nkb; ++j) {
+    const int st = j & 1;
+    const bool next = j + 1 < nkb;
+    wait_vm0();
+    __syncthreads();
+    const uint16_t* K = sK[st];
+    const uint16_t* V = sV[st];
+    // S^T = K Q^T for the two 32-key tiles; the next block's copy goes out
+    // between these MFMAs
+    f32x16 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = 32 * t + (lane & 31);
+        const int c = (2 * ks + (lane >> 5)) ^ (row & 15);
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(K, row, kAD / 8, c), qf[ks], s[t], 0, 0, 0);
+      }
+      if (next) copy_piece(j + 1, st ^ 1, ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // mask and online softmax (base 2)
+    const int kb0 = kKB * j;
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb0 + 32 * t + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const float v = key <= my_q ? s[t][r] * a.scale_log2 : -INFINITY;
+        s[t][r] = v;
+        bmax = fmaxf(bmax, v);
+      }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    const bool grow = bmax > mrun + kRescale;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mnew = grow ? bmax : mrun;
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);  // mrun = -inf at first: 0
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+      mrun = mnew;
+    }
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        u16x8 pk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(s[t][8 * uu + e] - mrun);
+          lsum += p;
+          pk[e] = f32_to_bf16(p);
+        }
+        pf[t][uu] = __builtin_bit_cast(bf16x8, pk);
+      }
+    // O^T += V^T P^T: 8 dim tiles, 4 steps of 16 keys (tile t, half uu)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int row = 32 * dt + (lane & 31);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = (2 * g + (lane >> 5)) ^ ((row >> 1) & 7);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(V, row, kKB / 8, c), pf[g >> 1][g & 1], o[dt], 0, 0, 0);
+      }
+    }
+  }
+  wait_vm0();
+
+  // out = O / l * sigmoid(gate): lane holds query my_q, dims 32 dt + 8 (r/4) + 4 (l/32) + r%4
+  lsum += __shfl_xor(lsum, 32, 64);
+  const float inv = 1.f / lsum;
+  const int qi = qw + (lane & 31);
+  if (qi < L) {
+    const size_t base = ((size_t)(s0 + qi) * a.Hq + h) * kAD + 4 * (lane >> 5);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const size_t at = base + 32 * dt + 8 * g4;
+        const u16x4 gr = *reinterpret_cast<const u16x4*>(a.gate + at);
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float z = bf16_to_f32(gr[e]);
+          y[e] = o[dt][4 * g4 + e] * inv * (1.f / (1.f + __expf(-z)));
+        }
+        *reinterpret_cast<u32x2*>(a.out + at) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_qk_prep(const AttnArgs& a, void* q_out, void* k_out, hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
+  PrepArgs pa{};
+  pa.q = static_cast<const uint16_t*>(a.q);
+  pa.k = static_cast<const uint16_t*>(a.k);
+  pa.q_w = a.q_norm_w;
+  pa.k_w = a.k_norm_w;
+  pa.cu = a.cu_seqlens;
+  pa.q_rot = static_cast<uint16_t*>(q_out);
+  pa.k_rot = static_cast<uint16_t*>(k_out);
+  pa.rows = a.T;
+  pa.N = a.N;
+  pa.Hq = a.Hq;
+  pa.Hk = a.Hk;
+  pa.eps = a.eps;
+  pa.base = a.rope_base;
+  hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)a.T), dim3(256), 0, st, pa);
+  return hipGetLastError();
+}
+
+size_t attn_prefill_workspace_bytes(const AttnArgs& a) {
+  const size_t T = a.T, N = a.N;
+  const size_t tpad = (size_t)kKB * ((T + kKB - 1) / kKB + N);
+  size_t b = ((2 * (N + 1)) * 4 + 255) / 256 * 256;
+  b += (T * a.Hq * kAD * 2 + 255) / 256 * 256;       // q_rot
+  b += (tpad * a.Hk * kAD * 2 + 255) / 256 * 256;    // k_pad
+  b += (tpad * a.Hk * kAD * 2 + 255) / 256 * 256;    // vt
+  return b;
+}
+
+hipError_t launch_attn_prefill(const AttnArgs& a, void* ws, hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
+  const size_t T = a.T, N = a.N;
+  const int64_t chunks = (int64_t)((T + kKB - 1) / kKB + N);
+  const int64_t tpad = kKB * chunks;
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  int32_t* table = reinterpret_cast<int32_t*>(p);
+  p += ((2 * (N + 1)) * 4 + 255) / 256 * 256;
+  uint16_t* q_rot = reinterpret_cast<uint16_t*>(p);
+  p += (T * a.Hq * kAD * 2 + 255) / 256 * 256;
+  uint16_t* k_pad = reinterpret_cast<uint16_t*>(p);
+  p += (tpad * a.Hk * kAD * 2 + 255) / 256 * 256;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(p);
+
+  hipLaunchKernelGGL(attn_table_kernel, dim3(1), dim3(256), 0, st, a.cu_seqlens, a.N, table);
+  PrepArgs pa{};
+  pa.q = static_cast<const uint16_t*>(a.q);
+  pa.k = static_cast<const uint16_t*>(a.k);
+  pa.v = static_cast<const uint16_t*>(a.v);
+  pa.q_w = a.q_norm_w;
+  pa.k_w = a.k_norm_w;
+  pa.cu = a.cu_seqlens;
+  pa.table = table;
+  pa.q_rot = q_rot;
+  pa.k_pad = k_pad;
+  pa.k_cache = static_cast<uint16_t*>(a.k_cache);
+  pa.v_cache = static_cast<uint16_t*>(a.v_cache);
+  pa.rows = a.T;
+  pa.N = a.N;
+  pa.Hq = a.Hq;
+  pa.Hk = a.Hk;
+  pa.cache_len = a.cache_len;
+  pa.eps = a.eps;
+  pa.base = a.rope_base;
+  hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)T), dim3(256), 0, st, pa);
+  hipLaunchKernelGGL(attn_vt_kernel, dim3((unsigned)chunks, (unsigned)a.Hk), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(a.v), a.cu_seqlens, table, a.N, a.Hk, tpad, vt);
+  FwdArgs f{};
+  f.q_rot = q_rot;
+  f.k_pad = k_pad;
+  f.vt = vt;
+  f.gate = static_cast<const uint16_t*>(a.gate);
+  f.cu = a.cu_seqlens;
+  f.table = table;
+  f.out = static_cast<uint16_t*>(a.out);
+  f.N = a.N;
+  f.Hq = a.Hq;
+  f.Hk = a.Hk;
+  f.tpad = tpad;
+  f.scale_log2 = 1.4426950408889634f / 16.f;
+  const int G = a.Hq / a.Hk;
+  const int64_t units = (int64_t)a.Hk * ((T + kQB - 1) / kQB + N);
+  const int64_t grid = (units + kXcds - 1) / kXcds * kXcds * G;
+  hipLaunchKernelGGL(attn_fwd_kernel, dim3((unsigned)grid), dim3(256), 0, st, f);
+  return hipGetLastError();
+}
+
+}  // namespace gdr

@@ -423,3 +423,73 @@ def delta_layer_fwd(hidden: torch.Tensor, w_in: torch.Tensor, conv_w: torch.Tens
                                          _stream(dev))
     _lib.check("gdr_delta_layer_fwd", st)
     return out, final_state, conv_state_out
+
+
+def attn_desc(T, N, Hq, Hk, D=256, cache_len=0, eps=1e-6, rope_base=1.0e7):
+    d = _lib.GdrAttnDesc()
+    d.struct_size = ctypes.sizeof(_lib.GdrAttnDesc)
+    d.num_tokens, d.num_seqs, d.num_q_heads, d.num_kv_heads, d.head_dim = T, N, Hq, Hk, D
+    d.cache_len, d.norm_eps, d.rope_base = cache_len, eps, rope_base
+    return d
+
+
+def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor, q_norm_w: torch.Tensor,
+                 k_norm_w: torch.Tensor, cu_seqlens: torch.Tensor, k_cache: Optional[torch.Tensor] = None,
+                 v_cache: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, eps: float = 1e-6, rope_base: float = 1.0e7):
+    """Causal global attention prefill (gdr_attn_prefill).
+
+    q, gate: [T, Hq, 256] bf16; k, v: [T, Hk, 256] bf16; norm weights [256]
+    fp32; cu_seqlens int32 [N+1]; optional k_cache / v_cache [N, L, Hk, 256]
+    bf16 receive the rotated keys and the values.  Returns out [T, Hq, 256] bf16.
+    """
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate")):
+        _need(t, name, (torch.bfloat16,), dev)
+    _need(q_norm_w, "q_norm_w", (torch.float32,), dev)
+    _need(k_norm_w, "k_norm_w", (torch.float32,), dev)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,), dev)
+    T, Hq, D = q.shape
+    Hk = k.shape[1]
+    if k.shape != (T, Hk, D) or v.shape != (T, Hk, D) or gate.shape != (T, Hq, D):
+        raise ValueError("shape mismatch among q, k, v, gate")
+    N = cu_seqlens.numel() - 1
+    cache_len = 0
+    if k_cache is not None:
+        _need(k_cache, "k_cache", (torch.bfloat16,), dev)
+        _need(v_cache, "v_cache", (torch.bfloat16,), dev)
+        cache_len = k_cache.shape[1]
+        if k_cache.shape != (N, cache_len, Hk, D) or v_cache.shape != k_cache.shape:
+            raise ValueError(f"caches must be [N, L, {Hk}, {D}]")
+    d = attn_desc(T, N, Hq, Hk, D, cache_len, eps, rope_base)
+    if workspace is None:
+        nb = ctypes.c_size_t(0)
+        _lib.check("gdr_attn_prefill_workspace_size",
+                   _lib.load().gdr_attn_prefill_workspace_size(ctypes.byref(d), ctypes.byref(nb)))
+        workspace = torch.empty(max(nb.value, 1), device=dev, dtype=torch.uint8)
+    if out is None:
+        out = torch.empty((T, Hq, D), device=dev, dtype=torch.bfloat16)
+    st = _lib.load().gdr_attn_prefill(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w),
+                                      _ptr(k_norm_w), _ptr(cu_seqlens), _ptr(out), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check("gdr_attn_prefill", st)
+    return out
+
+
+def attn_qk_norm_rope(q: torch.Tensor, k: torch.Tensor, q_norm_w: torch.Tensor, k_norm_w: torch.Tensor,
+                      cu_seqlens: torch.Tensor, eps: float = 1e-6, rope_base: float = 1.0e7):
+    """q' and k' (RMS norm + rotary) of a packed batch (gdr_attn_qk_norm_rope)."""
+    dev = q.device
+    _need(q, "q", (torch.bfloat16,), dev)
+    _need(k, "k", (torch.bfloat16,), dev)
+    _need(q_norm_w, "q_norm_w", (torch.float32,), dev)
+    _need(k_norm_w, "k_norm_w", (torch.float32,), dev)
+    _need(cu_seqlens, "cu_seqlens", (torch.int32,), dev)
+    T, Hq, D = q.shape
+    Hk = k.shape[1]
+    q_out, k_out = torch.empty_like(q), torch.empty_like(k)
+    d = attn_desc(T, cu_seqlens.numel() - 1, Hq, Hk, D, 0, eps, rope_base)
+    st = _lib.load().gdr_attn_qk_norm_rope(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(q_norm_w), _ptr(k_norm_w),
+                                           _ptr(cu_seqlens), _ptr(q_out), _ptr(k_out), _stream(dev))
+    _lib.check("gdr_attn_qk_norm_rope", st)
+    return q_out, k_out

@@ -46,6 +46,8 @@ __all__ = [
     "LayerInputs",
     "layer_inputs",
     "HIDDEN",
+    "AttnInputs",
+    "attn_inputs",
     "HK",
     "HV",
     "D",
@@ -300,3 +302,33 @@ def layer_inputs(seed: int = 6, *, lengths=(4096,), hk: int = HK, hv: int = HV, 
     norm_w = (1.0 + 0.1 * gen.standard_normal(d)).astype(np.float32)
     w_out = round_bf16(gen.standard_normal((hidden, V), dtype=np.float32) / np.float32(math.sqrt(V)))
     return LayerInputs(x, w_in, conv_w, A_log, dt_bias, norm_w, w_out, cu, hk, hv, d)
+
+
+ATTN_HQ, ATTN_HK, ATTN_D = 24, 4, 256  # the global attention layer's heads
+
+
+@dataclass
+class AttnInputs:
+    q: np.ndarray       # [T, Hq, D] bf16 values
+    k: np.ndarray       # [T, Hk, D]
+    v: np.ndarray       # [T, Hk, D]
+    gate: np.ndarray    # [T, Hq, D]
+    q_norm_w: np.ndarray  # [D]
+    k_norm_w: np.ndarray  # [D]
+    cu_seqlens: np.ndarray
+
+
+def attn_inputs(seed: int = 40, *, lengths=(4096,), hq: int = ATTN_HQ, hk: int = ATTN_HK,
+                d: int = ATTN_D) -> AttnInputs:
+    """Activations of the global attention layer: q, k, v and gate ~ N(0, 1)
+    (the outputs of its projections), norm weights 1 + 0.1 N(0, 1)."""
+    cu = cu_seqlens_of(list(lengths))
+    T = int(cu[-1])
+    gen = rng(seed, 30)
+    q = round_bf16(gen.standard_normal((T, hq, d), dtype=np.float32))
+    k = round_bf16(gen.standard_normal((T, hk, d), dtype=np.float32))
+    v = round_bf16(gen.standard_normal((T, hk, d), dtype=np.float32))
+    gate = round_bf16(gen.standard_normal((T, hq, d), dtype=np.float32))
+    qw = (1.0 + 0.1 * gen.standard_normal(d)).astype(np.float32)
+    kw = (1.0 + 0.1 * gen.standard_normal(d)).astype(np.float32)
+    return AttnInputs(q, k, v, gate, qw, kw, cu)

@@ -380,6 +380,69 @@ gdr_status gdr_delta_layer_fwd(const gdr_layer_desc* d, const void* hidden, cons
                                const float* initial_state, float* final_state, void* out, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * The global attention layer, every fourth layer of the hybrid decoder
+ * (deepmagic page, architecture section; kongchang page, attention details):
+ * grouped-query attention, 24 query / 4 key-value heads of dim 256, an RMS
+ * norm on q and on k, rotary encoding on the first 64 dims of each head
+ * (base 1e7), a sigmoid gate on the output.  For every query head h (key /
+ * value head h / (Hq / Hk)) and token t at position p inside its sequence:
+ *
+ *   q' = rot_p(rmsnorm(q_t,h) * q_norm_w),  k'_s = rot_s(rmsnorm(k_s) * k_norm_w)
+ *   out_t,h = softmax_s<=t(q' . k'_s / 16) v_s * sigmoid(gate_t,h)
+ *
+ * rmsnorm(x) = x / sqrt(mean(x^2) + eps) over the head's 256 dims; rot_p turns
+ * the pairs (j, j + 32), j < 32, of the first 64 dims by p * base^(-j/32) and
+ * leaves dims 64..255 alone.  q, k, v, gate and out are bf16; the norms and
+ * rotation run in fp32 (angles reduced in fp64) and round q', k' to bf16;
+ * scores and softmax are fp32; probabilities enter the value product as bf16.
+ * ------------------------------------------------------------------------ */
+
+typedef struct gdr_attn_desc {
+  uint32_t struct_size; /* sizeof(gdr_attn_desc) */
+  int32_t num_tokens;   /* prefill: T packed tokens; decode: N */
+  int32_t num_seqs;     /* N */
+  int32_t num_q_heads;  /* Hq (24) */
+  int32_t num_kv_heads; /* Hk (4), Hq a multiple of it */
+  int32_t head_dim;     /* 256 */
+  int32_t cache_len;    /* slots per sequence in k_cache / v_cache (0 without a cache) */
+  float norm_eps;       /* RMS norm epsilon (1e-6) */
+  double rope_base;     /* 1e7 */
+} gdr_attn_desc;
+
+/*
+ * The first step alone: q' and k' of every token of a packed batch
+ * (positions restart at 0 in each sequence).
+ *   q [T, Hq, 256], k [T, Hk, 256] bf16;  q_norm_w, k_norm_w [256] fp32
+ *   cu_seqlens [N+1] int32 device array;  q_out [T, Hq, 256], k_out [T, Hk, 256] bf16
+ * gdr_attn_prefill computes q' and k' with this same code.  Errors as
+ * gdr_attn_prefill.
+ */
+gdr_status gdr_attn_qk_norm_rope(const gdr_attn_desc* d, const void* q, const void* k, const float* q_norm_w,
+                                 const float* k_norm_w, const int32_t* cu_seqlens, void* q_out, void* k_out,
+                                 void* stream);
+
+/* Device workspace gdr_attn_prefill needs for *d, in bytes. */
+gdr_status gdr_attn_prefill_workspace_size(const gdr_attn_desc* d, size_t* bytes);
+
+/*
+ * Causal prefill over a packed batch:
+ *   q, gate      [T, Hq, 256] bf16;  k, v [T, Hk, 256] bf16
+ *   q_norm_w, k_norm_w [256] fp32
+ *   cu_seqlens   [N+1] int32 device array (positions restart at 0 in each sequence)
+ *   out          [T, Hq, 256] bf16
+ *   k_cache, v_cache  [N, cache_len, Hk, 256] bf16 or both NULL: when given,
+ *                slot p of sequence n receives its token p's k' and v, for
+ *                every p < cache_len (ready for gdr_attn_decode)
+ *   workspace    >= gdr_attn_prefill_workspace_size bytes, 256-byte aligned
+ * Errors: INVALID_ARG for NULL required pointers, misalignment (16 bytes),
+ * a short workspace, one cache pointer without the other; UNSUPPORTED unless
+ * head_dim = 256 and Hq is a multiple of Hk.
+ */
+gdr_status gdr_attn_prefill(const gdr_attn_desc* d, const void* q, const void* k, const void* v, const void* gate,
+                            const float* q_norm_w, const float* k_norm_w, const int32_t* cu_seqlens, void* out,
+                            void* k_cache, void* v_cache, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
