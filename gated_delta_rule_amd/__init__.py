@@ -6,6 +6,7 @@ if it has not been built (``python -m gated_delta_rule_amd.build``).
 """
 from ._lib import GDRError, load as load_library  # noqa: F401
 from .ops import (  # noqa: F401
+    attn_decode,
     attn_prefill,
     attn_qk_norm_rope,
     chunk_gated_delta_rule,
@@ -33,4 +34,5 @@ __all__ = [
     "delta_layer_workspace",
     "attn_prefill",
     "attn_qk_norm_rope",
+    "attn_decode",
 ]

@@ -33,6 +33,8 @@ EXPORTED = (
     "gdr_attn_qk_norm_rope",
     "gdr_attn_prefill_workspace_size",
     "gdr_attn_prefill",
+    "gdr_attn_decode_workspace_size",
+    "gdr_attn_decode",
 )
 
 
@@ -175,6 +177,10 @@ def load() -> ctypes.CDLL:
     lib.gdr_attn_prefill_workspace_size.argtypes = [ctypes.POINTER(GdrAttnDesc), ctypes.POINTER(SZ)]
     lib.gdr_attn_prefill.restype = I32
     lib.gdr_attn_prefill.argtypes = [ctypes.POINTER(GdrAttnDesc)] + [P] * 11 + [SZ, P]
+    lib.gdr_attn_decode_workspace_size.restype = I32
+    lib.gdr_attn_decode_workspace_size.argtypes = [ctypes.POINTER(GdrAttnDesc), ctypes.POINTER(SZ)]
+    lib.gdr_attn_decode.restype = I32
+    lib.gdr_attn_decode.argtypes = [ctypes.POINTER(GdrAttnDesc)] + [P] * 11 + [SZ, P]
     _lib = lib
     return lib
 

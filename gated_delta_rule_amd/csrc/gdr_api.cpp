@@ -603,7 +603,8 @@ gdr_status gdr_attn_prefill(const gdr_attn_desc* d, const void* q, const void* k
   if (d->num_tokens > 0 && (!q || !k || !v || !gate || !out))
     return fail(GDR_ERR_INVALID_ARG, "q, k, v, gate and out are required");
   if (!k_cache != !v_cache) return fail(GDR_ERR_INVALID_ARG, "give both k_cache and v_cache or neither");
-  if (k_cache && d->cache_len <= 0) return fail(GDR_ERR_INVALID_ARG, "a cache needs cache_len > 0");
+  if (k_cache && (d->cache_len <= 0 || d->cache_len % 64))
+    return fail(GDR_ERR_INVALID_ARG, "a cache needs cache_len > 0, a multiple of 64 (got %d)", d->cache_len);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(out) || !aligned16(k_cache) ||
       !aligned16(v_cache) || !aligned16(q_norm_w) || !aligned16(k_norm_w))
     return fail(GDR_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
@@ -623,6 +624,47 @@ gdr_status gdr_attn_prefill(const gdr_attn_desc* d, const void* q, const void* k
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   return hip_status(gdr::launch_attn_prefill(a, workspace, static_cast<hipStream_t>(stream)), "gdr_attn_prefill launch");
+}
+
+gdr_status gdr_attn_decode_workspace_size(const gdr_attn_desc* d, size_t* bytes) {
+  if (!bytes) return fail(GDR_ERR_INVALID_ARG, "bytes is NULL");
+  const gdr_status st = check_attn(d, true);
+  if (st != GDR_OK) return st;
+  if (d->cache_len <= 0 || d->cache_len % 64)
+    return fail(GDR_ERR_INVALID_ARG, "decode needs cache_len > 0, a multiple of 64 (got %d)", d->cache_len);
+  *bytes = gdr::attn_decode_workspace_bytes(attn_args(d));
+  return ok();
+}
+
+gdr_status gdr_attn_decode(const gdr_attn_desc* d, const void* q, const void* k, const void* v, const void* gate,
+                           const float* q_norm_w, const float* k_norm_w, void* k_cache, void* v_cache,
+                           const int32_t* cache_lens, void* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  gdr_status st = check_attn(d, true);
+  if (st != GDR_OK) return st;
+  if (d->cache_len <= 0 || d->cache_len % 64)
+    return fail(GDR_ERR_INVALID_ARG, "decode needs cache_len > 0, a multiple of 64 (got %d)", d->cache_len);
+  if (!q || !k || !v || !gate || !q_norm_w || !k_norm_w || !k_cache || !v_cache || !cache_lens || !out)
+    return fail(GDR_ERR_INVALID_ARG, "q, k, v, gate, norm weights, caches, cache_lens and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(out) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(q_norm_w) || !aligned16(k_norm_w))
+    return fail(GDR_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  gdr::AttnArgs a = attn_args(d);
+  const size_t need = gdr::attn_decode_workspace_bytes(a);
+  if (!workspace || workspace_bytes < need)
+    return fail(GDR_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace ? workspace_bytes : 0);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GDR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.gate = gate;
+  a.q_norm_w = q_norm_w;
+  a.k_norm_w = k_norm_w;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cache_lens = cache_lens;
+  a.out = out;
+  return hip_status(gdr::launch_attn_decode(a, workspace, static_cast<hipStream_t>(stream)), "gdr_attn_decode launch");
 }
 
 }  // extern "C"

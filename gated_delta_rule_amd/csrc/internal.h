@@ -100,7 +100,7 @@ struct AttnArgs {
   const int32_t* cu_seqlens;       // prefill [N+1]
   const int32_t* cache_lens;       // decode [N]: cached tokens before this one
   void* out;                       // [rows, Hq, 256] bf16
-  void *k_cache, *v_cache;         // [N, cache_len, Hk, 256] bf16 or NULL (prefill)
+  void *k_cache, *v_cache;         // [N, cache_len, Hk, 256] and [N, Hk, 256, cache_len] bf16, or NULL (prefill)
   int cache_len;
   int T, N, Hq, Hk;                // T: packed tokens (prefill) or N (decode)
   float eps;
@@ -111,6 +111,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_linear(const LinearArgs& a, hipStream_t st);
 size_t attn_prefill_workspace_bytes(const AttnArgs& a);
 hipError_t launch_attn_qk_prep(const AttnArgs& a, void* q_out, void* k_out, hipStream_t st);
+size_t attn_decode_workspace_bytes(const AttnArgs& a);
+hipError_t launch_attn_decode(const AttnArgs& a, void* workspace, hipStream_t st);
 hipError_t launch_attn_prefill(const AttnArgs& a, void* workspace, hipStream_t st);
 hipError_t launch_decode_layer(const LayerStepArgs& a, hipStream_t st);
 hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t st);

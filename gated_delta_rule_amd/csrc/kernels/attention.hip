@@ -184,8 +184,13 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
       if (to_cache) {
         const size_t c = ((size_t)n * a.cache_len + pos) * a.Hk + h;
         *reinterpret_cast<u32x2*>(a.k_cache + c * kAD + 4 * lane) = out;
-        *reinterpret_cast<u16x4*>(a.v_cache + c * kAD + 4 * lane) =
-            *reinterpret_cast<const u16x4*>(a.v + ((size_t)t * a.Hk + h) * kAD + 4 * lane);
+        if (!a.cu) {
+          // decode: the token's v into the transposed cache, one key column
+          const u16x4 vv = *reinterpret_cast<const u16x4*>(a.v + ((size_t)t * a.Hk + h) * kAD + 4 * lane);
+          uint16_t* vc = a.v_cache + (((size_t)n * a.Hk + h) * kAD + 4 * lane) * a.cache_len + pos;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vc[(size_t)e * a.cache_len] = vv[e];
+        }
       }
     }
   }
@@ -202,7 +207,8 @@ __device__ __forceinline__ int kperm(int i) {
 }
 
 __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* v, const int32_t* cu, const int32_t* table,
-                                                      int N, int Hk, int64_t tpad, uint16_t* vt) {
+                                                      int N, int Hk, int64_t tpad, uint16_t* vt, uint16_t* v_cache,
+                                                      int cache_len) {
   __shared__ uint16_t tile[kKB][kAD + 2];
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   if (c >= table[N]) return;
@@ -227,6 +233,23 @@ __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* v, const i
 #pragma unroll
     for (int e = 0; e < 8; ++e) pk[e] = row[s + e];
     *reinterpret_cast<u16x8*>(dst + s) = pk;
+  }
+  if (v_cache) {
+    // [N, Hk, D, cache_len]: this chunk's keys k0 .. k0+63 of row d, natural
+    // order, only positions inside the sequence and the cache
+    uint16_t* vc = v_cache + (((size_t)n * Hk + h) * kAD + d) * cache_len;
+    const int kend = min(L, cache_len) - k0;
+    if (kend >= kKB) {
+#pragma unroll
+      for (int s = 0; s < kKB; s += 8) {
+        u16x8 pk;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pk[e] = tile[s + e][d];
+        *reinterpret_cast<u16x8*>(vc + k0 + s) = pk;
+      }
+    } else {
+      for (int s = 0; s < kend; ++s) vc[k0 + s] = tile[s][d];
+    }
   }
 }
 
@@ -417,7 +440,218 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode: one query token per sequence against its cache.  Each wave takes
+// one 256-key split of one (sequence, kv head) and the G query heads that
+// read it, with no LDS: its MFMA operands come straight from the caches
+// (K [N, L, Hk, D] rows, V^T [N, Hk, D, L] rows, both 16 bytes per lane).
+//   S^T = K Q^T   query columns = the G heads (the other lanes' columns are
+//                 zero), 32-key tiles as in the prefill
+//   softmax as in the prefill; the probabilities are put back in natural key
+//   order with two lane exchanges per 16 keys (the prefill instead permutes
+//   its V^T copy)
+//   O^T += V^T P^T
+// The split's running maximum, sum and unnormalised output go to a
+// workspace; attn_combine_kernel merges the splits and applies the gate.
+constexpr int kDecSplit = 256;
+
+struct DecArgs {
+  const uint16_t* q_rot;        // [N, Hq, D]
+  const uint16_t *k_cache, *v_cache;
+  const int32_t* cache_lens;    // [N]; this step's token sits at cache_lens[n]
+  float* part;                  // [N, Hk, nsplit, G, D + 2]
+  int N, Hq, Hk, cache_len, nsplit;
+  float scale_log2;
+};
+
+__global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int split = gw % a.nsplit, nk = gw / a.nsplit;
+  const int kvh = nk % a.Hk, n = nk / a.Hk;
+  if (n >= a.N) return;
+  const int G = a.Hq / a.Hk;
+  const int len = a.cache_lens[n] + 1;
+  const int kb = split * kDecSplit;
+  const int col = lane & 31, hf = lane >> 5;
+  float* part = a.part + ((((size_t)n * a.Hk + kvh) * a.nsplit + split) * G) * (kAD + 2);
+  if (kb >= len) {
+    if (col < G && hf == 0) {
+      part[col * (kAD + 2) + kAD] = -INFINITY;
+      part[col * (kAD + 2) + kAD + 1] = 0.f;
+    }
+    return;
+  }
+  bf16x8 qf[16];
+  {
+    const uint16_t* qrow = a.q_rot + ((size_t)n * a.Hq + kvh * G + min(col, G - 1)) * kAD + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+      if (col >= G) qf[ks] = bf16x8{};
+    }
+  }
+  f32x16 o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+  float mrun = -INFINITY, lsum = 0.f;
+  const uint16_t* kbase = a.k_cache + ((size_t)n * a.cache_len * a.Hk + kvh) * kAD + 8 * hf;
+  const uint16_t* vbase = a.v_cache + ((size_t)n * a.Hk + kvh) * kAD * a.cache_len + 8 * hf;
+  const int kend = min(kb + kDecSplit, len);
+  for (int k0 = kb; k0 < kend; k0 += kKB) {
+    f32x16 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
+      const uint16_t* krow = kbase + (size_t)(k0 + 32 * t + col) * a.Hk * kAD;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks)
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(krow + 16 * ks), qf[ks], s[t],
+                                                       0, 0, 0);
+    }
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const float v = key < len ? s[t][r] * a.scale_log2 : -INFINITY;
+        s[t][r] = v;
+        bmax = fmaxf(bmax, v);
+      }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
+    const bool grow = bmax > mrun + kRescale;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float mnew = grow ? bmax : mrun;
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      lsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+      mrun = mnew;
+    }
+    // probabilities, then natural key order: lane half hf holds keys
+    // {4 hf .. 4 hf + 3, 8 + 4 hf .. 8 + 4 hf + 3} of each 16; after the
+    // exchange it holds 8 hf .. 8 hf + 7
+    bf16x8 pf[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t d[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + 2 * e] - mrun);
+        const float p1 = __builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + 2 * e + 1] - mrun);
+        lsum += p0 + p1;
+        d[e] = pack_bf16x2(p0, p1);
+      }
+      const uint32_t x0 = __shfl_xor(hf ? d[0] : d[2], 32, 64);
+      const uint32_t x1 = __shfl_xor(hf ? d[1] : d[3], 32, 64);
+      const u32x4 nat = hf ? u32x4{x0, x1, d[2], d[3]} : u32x4{d[0], d[1], x0, x1};
+      pf[g] = __builtin_bit_cast(bf16x8, nat);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint16_t* vrow = vbase + (size_t)(32 * dt + col) * a.cache_len + k0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vrow + 16 * g), pf[g], o[dt],
+                                                        0, 0, 0);
+    }
+  }
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (col < G) {
+    float* pr = part + col * (kAD + 2);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(pr + 32 * dt + 8 * g4 + 4 * hf) =
+            f32x4{o[dt][4 * g4], o[dt][4 * g4 + 1], o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]};
+    if (hf == 0) {
+      pr[kAD] = mrun;
+      pr[kAD + 1] = lsum;
+    }
+  }
+}
+
+// Merge of the splits of one (sequence, query head), one thread per dim:
+// out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s * sigmoid(gate).
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* part, const uint16_t* gate,
+                                                           const int32_t* cache_lens, uint16_t* out, int Hq, int Hk,
+                                                           int nsplit) {
+  const int n = blockIdx.x / Hq, h = blockIdx.x % Hq, d = threadIdx.x;
+  const int G = Hq / Hk, kvh = h / G, c = h % G;
+  const int used = (cache_lens[n] + 1 + kDecSplit - 1) / kDecSplit;
+  const float* p = part + (((size_t)n * Hk + kvh) * nsplit * G + c) * (kAD + 2);
+  const size_t stride = (size_t)G * (kAD + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < used; ++s) M = fmaxf(M, p[s * stride + kAD]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < used; ++s) {
+    const float w = __builtin_amdgcn_exp2f(p[s * stride + kAD] - M);
+    num += w * p[s * stride + d];
+    den += w * p[s * stride + kAD + 1];
+  }
+  const size_t at = ((size_t)n * Hq + h) * kAD + d;
+  const float z = bf16_to_f32(gate[at]);
+  out[at] = f32_to_bf16(num / den * (1.f / (1.f + __expf(-z))));
+}
+
 }  // namespace
+
+size_t attn_decode_workspace_bytes(const AttnArgs& a) {
+  const size_t nsplit = (a.cache_len + kDecSplit - 1) / kDecSplit;
+  const size_t q = ((size_t)a.N * a.Hq * kAD * 2 + 255) / 256 * 256;
+  return q + (size_t)a.N * a.Hk * nsplit * (a.Hq / a.Hk) * (kAD + 2) * 4;
+}
+
+hipError_t launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st) {
+  if (a.N == 0) return hipSuccess;
+  const int nsplit = (a.cache_len + kDecSplit - 1) / kDecSplit;
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  uint16_t* q_rot = reinterpret_cast<uint16_t*>(p);
+  float* part = reinterpret_cast<float*>(p + ((size_t)a.N * a.Hq * kAD * 2 + 255) / 256 * 256);
+  PrepArgs pa{};
+  pa.q = static_cast<const uint16_t*>(a.q);
+  pa.k = static_cast<const uint16_t*>(a.k);
+  pa.v = static_cast<const uint16_t*>(a.v);
+  pa.q_w = a.q_norm_w;
+  pa.k_w = a.k_norm_w;
+  pa.cache_lens = a.cache_lens;
+  pa.q_rot = q_rot;
+  pa.k_cache = static_cast<uint16_t*>(a.k_cache);
+  pa.v_cache = static_cast<uint16_t*>(a.v_cache);
+  pa.rows = a.N;
+  pa.N = a.N;
+  pa.Hq = a.Hq;
+  pa.Hk = a.Hk;
+  pa.cache_len = a.cache_len;
+  pa.eps = a.eps;
+  pa.base = a.rope_base;
+  hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)a.N), dim3(256), 0, st, pa);
+  DecArgs d{};
+  d.q_rot = q_rot;
+  d.k_cache = static_cast<const uint16_t*>(a.k_cache);
+  d.v_cache = static_cast<const uint16_t*>(a.v_cache);
+  d.cache_lens = a.cache_lens;
+  d.part = part;
+  d.N = a.N;
+  d.Hq = a.Hq;
+  d.Hk = a.Hk;
+  d.cache_len = a.cache_len;
+  d.nsplit = nsplit;
+  d.scale_log2 = 1.4426950408889634f / 16.f;
+  const int64_t waves = (int64_t)a.N * a.Hk * nsplit;
+  hipLaunchKernelGGL(attn_decode_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, d);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.N * a.Hq)), dim3(256), 0, st, part,
+                     static_cast<const uint16_t*>(a.gate), a.cache_lens, static_cast<uint16_t*>(a.out), a.Hq, a.Hk,
+                     nsplit);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_qk_prep(const AttnArgs& a, void* q_out, void* k_out, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
@@ -485,7 +719,8 @@ hipError_t launch_attn_prefill(const AttnArgs& a, void* ws, hipStream_t st) {
   pa.base = a.rope_base;
   hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)T), dim3(256), 0, st, pa);
   hipLaunchKernelGGL(attn_vt_kernel, dim3((unsigned)chunks, (unsigned)a.Hk), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(a.v), a.cu_seqlens, table, a.N, a.Hk, tpad, vt);
+                     static_cast<const uint16_t*>(a.v), a.cu_seqlens, table, a.N, a.Hk, tpad, vt,
+                     static_cast<uint16_t*>(a.v_cache), a.cache_len);
   FwdArgs f{};
   f.q_rot = q_rot;
   f.k_pad = k_pad;

@@ -440,8 +440,9 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.
     """Causal global attention prefill (gdr_attn_prefill).
 
     q, gate: [T, Hq, 256] bf16; k, v: [T, Hk, 256] bf16; norm weights [256]
-    fp32; cu_seqlens int32 [N+1]; optional k_cache / v_cache [N, L, Hk, 256]
-    bf16 receive the rotated keys and the values.  Returns out [T, Hq, 256] bf16.
+    fp32; cu_seqlens int32 [N+1]; optional k_cache [N, L, Hk, 256] and
+    v_cache [N, Hk, 256, L] bf16 (L a multiple of 64) receive the rotated keys
+    and the values.  Returns out [T, Hq, 256] bf16.
     """
     dev = q.device
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate")):
@@ -459,8 +460,8 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.
         _need(k_cache, "k_cache", (torch.bfloat16,), dev)
         _need(v_cache, "v_cache", (torch.bfloat16,), dev)
         cache_len = k_cache.shape[1]
-        if k_cache.shape != (N, cache_len, Hk, D) or v_cache.shape != k_cache.shape:
-            raise ValueError(f"caches must be [N, L, {Hk}, {D}]")
+        if k_cache.shape != (N, cache_len, Hk, D) or v_cache.shape != (N, Hk, D, cache_len):
+            raise ValueError(f"caches must be [N, L, {Hk}, {D}] and [N, {Hk}, {D}, L]")
     d = attn_desc(T, N, Hq, Hk, D, cache_len, eps, rope_base)
     if workspace is None:
         nb = ctypes.c_size_t(0)
@@ -493,3 +494,40 @@ def attn_qk_norm_rope(q: torch.Tensor, k: torch.Tensor, q_norm_w: torch.Tensor, 
                                            _ptr(cu_seqlens), _ptr(q_out), _ptr(k_out), _stream(dev))
     _lib.check("gdr_attn_qk_norm_rope", st)
     return q_out, k_out
+
+
+def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.Tensor, q_norm_w: torch.Tensor,
+                k_norm_w: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, cache_lens: torch.Tensor,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                rope_base: float = 1.0e7):
+    """One decode token per sequence (gdr_attn_decode).
+
+    q, gate: [N, Hq, 256]; k, v: [N, Hk, 256] bf16; k_cache [N, L, Hk, 256],
+    v_cache [N, Hk, 256, L] bf16 updated in place at cache_lens[n];
+    cache_lens int32 [N] (not advanced).  Returns out [N, Hq, 256] bf16.
+    """
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, name, (torch.bfloat16,), dev)
+    _need(q_norm_w, "q_norm_w", (torch.float32,), dev)
+    _need(k_norm_w, "k_norm_w", (torch.float32,), dev)
+    _need(cache_lens, "cache_lens", (torch.int32,), dev)
+    N, Hq, D = q.shape
+    Hk = k.shape[1]
+    L = k_cache.shape[1]
+    if k.shape != (N, Hk, D) or v.shape != (N, Hk, D) or gate.shape != (N, Hq, D) \
+            or k_cache.shape != (N, L, Hk, D) or v_cache.shape != (N, Hk, D, L) or cache_lens.shape != (N,):
+        raise ValueError("shape mismatch in attention decode inputs")
+    d = attn_desc(N, N, Hq, Hk, D, L, eps, rope_base)
+    if workspace is None:
+        nb = ctypes.c_size_t(0)
+        _lib.check("gdr_attn_decode_workspace_size",
+                   _lib.load().gdr_attn_decode_workspace_size(ctypes.byref(d), ctypes.byref(nb)))
+        workspace = torch.empty(max(nb.value, 1), device=dev, dtype=torch.uint8)
+    if out is None:
+        out = torch.empty((N, Hq, D), device=dev, dtype=torch.bfloat16)
+    st = _lib.load().gdr_attn_decode(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w),
+                                     _ptr(k_norm_w), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens), _ptr(out),
+                                     _ptr(workspace), workspace.numel(), _stream(dev))
+    _lib.check("gdr_attn_decode", st)
+    return out

@@ -72,8 +72,9 @@ def test_prefill_against_oracle(lengths, hq, hk):
     L = max(lengths) + 3
     say(f"attention prefill lengths {lengths} Hq={hq} Hk={hk}")
     q, k, v, g, qw, kw, cu = _dev(x, dev)
+    L = (L + 63) // 64 * 64
     kc = torch.zeros((N, L, hk, 256), device=dev, dtype=torch.bfloat16)
-    vc = torch.zeros_like(kc)
+    vc = torch.zeros((N, hk, 256, L), device=dev, dtype=torch.bfloat16)
     out = gdr.attn_prefill(q, k, v, g, qw, kw, cu, k_cache=kc, v_cache=vc)
     qo, ko = gdr.attn_qk_norm_rope(q, k, qw, kw, cu)
     torch.cuda.synchronize()
@@ -82,8 +83,8 @@ def test_prefill_against_oracle(lengths, hq, hk):
     for n in range(N):
         a, b = x.cu_seqlens[n], x.cu_seqlens[n + 1]
         assert bits_equal(kc[n, :b - a], ko[a:b])
-        assert bits_equal(vc[n, :b - a], v[a:b])
-        assert not torch.any(kc[n, b - a:].float() != 0)
+        assert bits_equal(vc[n, :, :, :b - a], v[a:b].permute(1, 2, 0).contiguous())
+        assert not torch.any(kc[n, b - a:].float() != 0) and not torch.any(vc[n, :, :, b - a:].float() != 0)
 
 
 def test_prefill_full_size_sampled():
@@ -120,3 +121,104 @@ def test_prefill_deterministic_and_finite():
     torch.cuda.synchronize()
     assert bits_equal(a, b)
     assert torch.isfinite(a.float()).all()
+
+
+def _gpu_qrot_at(q_row, k_row, qw, kw, pos, dev):
+    """The library's q' and k' of one token at position pos: the same kernel
+    run on a sequence whose last token is that one."""
+    import gated_delta_rule_amd as gdr
+    import torch
+    Hq, D = q_row.shape
+    Hk = k_row.shape[0]
+    qf = torch.zeros((pos + 1, Hq, D), device=dev, dtype=torch.bfloat16)
+    kf = torch.zeros((pos + 1, Hk, D), device=dev, dtype=torch.bfloat16)
+    qf[pos], kf[pos] = q_row, k_row
+    cu = torch.tensor([0, pos + 1], device=dev, dtype=torch.int32)
+    qo, ko = gdr.attn_qk_norm_rope(qf, kf, qw, kw, cu)
+    return qo[pos], ko[pos]
+
+
+@pytest.mark.parametrize("lens,L,hq,hk", [((0, 1, 255, 256, 1000), 1024, 24, 4), ((63, 64, 65), 128, 8, 2)])
+def test_decode_against_oracle(lens, L, hq, hk):
+    """One token per sequence against caches of different fill (empty, one
+    split, exactly a split, several): the token's k' and v land at its
+    position, nothing else in the caches moves, and the output is within
+    its bound of the oracle run on the GPU's q' and caches."""
+    import gated_delta_rule_amd as gdr
+    import torch
+    dev = gpu()
+    N = len(lens)
+    x = synth.attn_inputs(46, lengths=(1,) * N, hq=hq, hk=hk)
+    rng = synth.rng(47)
+    kc0 = synth.round_bf16(rng.standard_normal((N, L, hk, 256)))
+    vc0 = synth.round_bf16(rng.standard_normal((N, hk, 256, L)))
+    say(f"attention decode lens {lens} L={L} Hq={hq} Hk={hk}")
+    q, k, v, g, qw, kw, _ = _dev(x, dev)
+    kc, vc = to_dev(kc0, "bf16", dev), to_dev(vc0, "bf16", dev)
+    cl = torch.tensor(lens, device=dev, dtype=torch.int32)
+    out = gdr.attn_decode(q, k, v, g, qw, kw, kc, vc, cl)
+    torch.cuda.synchronize()
+    kch, vch = to_host(kc), to_host(vc)
+    qrot = np.zeros((N, hq, 256))
+    for n, p in enumerate(lens):
+        qg, kg = _gpu_qrot_at(q[n], k[n], qw, kw, p, dev)
+        qrot[n] = to_host(qg)
+        assert bits_equal(kc[n, p], kg)
+        assert np.array_equal(vch[n, :, :, p], to_host(v[n]))
+        keep = np.ones(L, bool)
+        keep[p] = False
+        assert np.array_equal(kch[n, keep], kc0[n, keep]) and np.array_equal(vch[n][..., keep], vc0[n][..., keep])
+    r = aref.core_decode(qrot, x.gate, kch, vch.transpose(0, 3, 1, 2), np.asarray(lens) + 1)
+    _check_out(to_host(out), r["out"], r["mass"])
+
+
+def test_decode_continues_prefill():
+    """Prefill 700 tokens into the caches, then decode tokens 700 and 701:
+    each output matches the oracle on the full causal prefix."""
+    import gated_delta_rule_amd as gdr
+    import torch
+    dev = gpu()
+    T, L = 702, 768
+    x = synth.attn_inputs(48, lengths=(T,))
+    q, k, v, g, qw, kw, _ = _dev(x, dev)
+    say("attention prefill 700 then decode 2")
+    kc = torch.zeros((1, L, 4, 256), device=dev, dtype=torch.bfloat16)
+    vc = torch.zeros((1, 4, 256, L), device=dev, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 700], device=dev, dtype=torch.int32)
+    gdr.attn_prefill(q[:700], k[:700], v[:700], g[:700], qw, kw, cu, k_cache=kc, v_cache=vc)
+    outs = []
+    for t in (700, 701):
+        cl = torch.tensor([t], device=dev, dtype=torch.int32)
+        outs.append(gdr.attn_decode(q[t:t + 1], k[t:t + 1], v[t:t + 1], g[t:t + 1], qw, kw, kc, vc, cl))
+    torch.cuda.synchronize()
+    qo, ko = gdr.attn_qk_norm_rope(q, k, qw, kw, torch.tensor([0, T], device=dev, dtype=torch.int32))
+    assert bits_equal(kc[0, :T], ko)
+    r = aref.core_prefill(to_host(qo), to_host(ko), x.v, x.gate, x.cu_seqlens, rows=[700, 701])
+    for i, t in enumerate((700, 701)):
+        _check_out(to_host(outs[i])[0], r["out"][t], r["mass"][t])
+
+
+def test_decode_full_size_sampled():
+    """64 sequences with 32768-slot caches filled to 32000 .. 32767 tokens (the
+    serving shape of the layer): 3 sequences checked on every head."""
+    import gated_delta_rule_amd as gdr
+    import torch
+    dev = gpu()
+    N, L = 64, 32768
+    say("attention decode full size N=64 L=32768")
+    gen = torch.Generator(device=dev).manual_seed(49)
+    kc = torch.randn((N, L, 4, 256), device=dev, generator=gen).to(torch.bfloat16)
+    vc = torch.randn((N, 4, 256, L), device=dev, generator=gen).to(torch.bfloat16)
+    x = synth.attn_inputs(50, lengths=(1,) * N)
+    q, k, v, g, qw, kw, _ = _dev(x, dev)
+    lens = np.asarray(synth.rng(51).integers(32000, L, size=N), dtype=np.int32)
+    cl = torch.as_tensor(lens, device=dev)
+    out = gdr.attn_decode(q, k, v, g, qw, kw, kc, vc, cl)
+    torch.cuda.synchronize()
+    for n in (0, 31, 63):
+        p = int(lens[n])
+        qg, _ = _gpu_qrot_at(q[n], k[n], qw, kw, p, dev)
+        kn = to_host(kc[n:n + 1, :p + 1])
+        vn = to_host(vc[n:n + 1, :, :, :p + 1]).transpose(0, 3, 1, 2)
+        r = aref.core_decode(to_host(qg)[None], x.gate[n:n + 1], kn, vn, np.array([p + 1]))
+        _check_out(to_host(out[n:n + 1]), r["out"], r["mass"])
