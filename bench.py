@@ -19,6 +19,9 @@ in the same run:
   layer     -- one whole delta layer on a 32768-token sequence with synthetic
                weights: in-projection GEMM, the path, out-projection GEMM
                (hidden 5120); stage times and the GEMMs' matrix-core rate
+  attention -- the global attention layer (24/4 heads, d 256): causal prefill
+               of a 32768-token sequence (matrix-core rate) and one decode
+               token for 64 sequences against 32768-slot KV caches (HBM rate)
   roofline  -- the dominant kernel of the call, the state-carrying
                recurrence (gdr_chunk_fwd_recurrence): its algorithmic HBM bytes
                per launch (q, k, v read, o written, state in and out) over its
@@ -35,7 +38,7 @@ in the same run:
                and 4 decode steps for the decode leg)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--pieces P] [--no-cpu]
-                       [--only prefill|decode|decode_layer|pipeline|layer|copy|roofline|all]
+                       [--only prefill|decode|decode_layer|pipeline|layer|attention|copy|roofline|all]
 """
 from __future__ import annotations
 
@@ -432,6 +435,77 @@ def bench_layer(reps: int = 5):
                         "weights": "synthetic, N(0, 1/fan_in)"})
 
 
+def bench_attention(reps: int = 3, dec_steps: int = 20):
+    """The global attention layer (24 query / 4 kv heads, d 256): causal
+    prefill of one 32768-token sequence (q/k norm + rotary, attention, gate),
+    as matrix-core work 4 Hq d T^2 / 2 against the bf16 peak, beside torch's
+    scaled_dot_product_attention on the same shapes (no norm, rotary or
+    gate); and one decode token for 64 sequences against 32768-slot caches
+    filled to 32 000+ tokens, as KV-cache bytes read per step against HBM."""
+    import torch
+    import gated_delta_rule_amd as gdr
+    from gated_delta_rule_amd import synth
+    dev = torch.device("cuda:0")
+    Hq, Hk, Da = synth.ATTN_HQ, synth.ATTN_HK, synth.ATTN_D
+    T = T_CALL
+    log(f"attention: prefill T={T}, decode N=64 x 32768-slot caches")
+    gen = torch.Generator(device=dev).manual_seed(52)
+    rnd = lambda *sh: torch.randn(sh, device=dev, generator=gen).to(torch.bfloat16)
+    q, k, v, g = rnd(T, Hq, Da), rnd(T, Hk, Da), rnd(T, Hk, Da), rnd(T, Hq, Da)
+    w = torch.ones(Da, device=dev)
+    cu = torch.tensor([0, T], device=dev, dtype=torch.int32)
+    out = torch.empty_like(q)
+    d = gdr.ops.attn_desc(T, 1, Hq, Hk, Da)
+    import ctypes
+    nb = ctypes.c_size_t(0)
+    gdr.load_library().gdr_attn_prefill_workspace_size(ctypes.byref(d), ctypes.byref(nb))
+    ws = torch.empty(nb.value, device=dev, dtype=torch.uint8)
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        s0, s1 = _events()
+        s0.record()
+        for _ in range(n):
+            fn()
+        s1.record()
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / n
+
+    ms = timed(lambda: gdr.attn_prefill(q, k, v, g, w, w, cu, out=out, workspace=ws), reps)
+    flop = 4.0 * Hq * Da * T * T / 2
+    qq = q.permute(1, 0, 2).unsqueeze(0)
+    kk = k.permute(1, 0, 2).unsqueeze(0).repeat_interleave(Hq // Hk, dim=1)
+    vv = v.permute(1, 0, 2).unsqueeze(0).repeat_interleave(Hq // Hk, dim=1)
+    try:
+        ms_ref = timed(lambda: torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, is_causal=True), reps)
+    except Exception:  # a reference only
+        ms_ref = None
+    del qq, kk, vv, q, k, v, g, out, ws
+
+    N, L = 64, 32768
+    kc = torch.randn((N, L, Hk, Da), device=dev, generator=gen).to(torch.bfloat16)
+    vc = torch.randn((N, Hk, Da, L), device=dev, generator=gen).to(torch.bfloat16)
+    lens = torch.randint(32000, L - dec_steps, (N,), device=dev, generator=gen, dtype=torch.int32)
+    qd, kd, vd, gd = rnd(N, Hq, Da), rnd(N, Hk, Da), rnd(N, Hk, Da), rnd(N, Hq, Da)
+    od = torch.empty_like(qd)
+    dd = gdr.ops.attn_desc(N, N, Hq, Hk, Da, L)
+    gdr.load_library().gdr_attn_decode_workspace_size(ctypes.byref(dd), ctypes.byref(nb))
+    wsd = torch.empty(nb.value, device=dev, dtype=torch.uint8)
+    ms_dec = timed(lambda: gdr.attn_decode(qd, kd, vd, gd, w, w, kc, vc, lens, out=od, workspace=wsd), dec_steps)
+    cache_bytes = float((lens.to(torch.int64) + 1).sum().item()) * Hk * Da * 2 * 2
+    return dict(prefill={"T": T, "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+                         "TFLOPs": flop / (ms * 1e-3) / 1e12,
+                         "frac_bf16_peak": flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                         "torch_sdpa_ms": ms_ref},
+                decode={"N": N, "cache_len": L, "us_per_step": ms_dec * 1e3,
+                        "kv_GBps": cache_bytes / (ms_dec * 1e-3) / 1e9,
+                        "frac_hbm": cache_bytes / (ms_dec * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                config={"num_q_heads": Hq, "num_kv_heads": Hk, "head_dim": Da, "rotary_dims": 64,
+                        "rope_base": 1e7})
+
+
 def bench_copy(n_bytes: int = 1 << 30, reps: int = 5):
     """Plain device copy of known size: calibration of the HBM byte counters."""
     import torch
@@ -519,7 +593,7 @@ def main():
     ap.add_argument("--steps", type=int, default=24)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--only", default="all", choices=["all", "prefill", "decode", "decode_layer", "pipeline", "layer",
-                                                      "copy", "roofline"])
+                                                      "attention", "copy", "roofline"])
     ap.add_argument("--pieces", type=int, default=N_CALLS,
                     help="distinct 32K pieces of the context to cycle through (8 = the whole 262144 tokens)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -599,6 +673,8 @@ def main():
         out["pipeline"] = bench_pipeline()
     if args.only in ("all", "layer"):
         out["layer"] = bench_layer()
+    if args.only in ("all", "attention"):
+        out["attention"] = bench_attention()
     if args.only == "all":
         ach = bench_roofline()
         out["achievable"] = ach
