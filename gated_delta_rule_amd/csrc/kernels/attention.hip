@@ -442,7 +442,7 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Decode: one query token per sequence against its cache.  Each wave takes
-// one 256-key split of one (sequence, kv head) and the G query heads that
+// one split (256 .. 2048 keys) of one (sequence, kv head) and the G query heads that
 // read it, with no LDS: its MFMA operands come straight from the caches
 // (K [N, L, Hk, D] rows, V^T [N, Hk, D, L] rows, both 16 bytes per lane).
 //   S^T = K Q^T   query columns = the G heads (the other lanes' columns are
@@ -453,14 +453,20 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
 //   O^T += V^T P^T
 // The split's running maximum, sum and unnormalised output go to a
 // workspace; attn_combine_kernel merges the splits and applies the gate.
-constexpr int kDecSplit = 256;
+// Keys per split: 256 .. 2048 (a multiple of 64), chosen on the host so that
+// a step has about 4096 waves.
+__host__ __device__ inline int dec_split_keys(int N, int Hk, int cache_len) {
+  int s = 256;
+  while (s < 2048 && (int64_t)N * Hk * ((cache_len + 2 * s - 1) / (2 * s)) >= 4096) s *= 2;
+  return s;
+}
 
 struct DecArgs {
   const uint16_t* q_rot;        // [N, Hq, D]
   const uint16_t *k_cache, *v_cache;
   const int32_t* cache_lens;    // [N]; this step's token sits at cache_lens[n]
   float* part;                  // [N, Hk, nsplit, G, D + 2]
-  int N, Hq, Hk, cache_len, nsplit;
+  int N, Hq, Hk, cache_len, nsplit, split_keys;
   float scale_log2;
 };
 
@@ -472,7 +478,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   if (n >= a.N) return;
   const int G = a.Hq / a.Hk;
   const int len = a.cache_lens[n] + 1;
-  const int kb = split * kDecSplit;
+  const int kb = split * a.split_keys;
   const int col = lane & 31, hf = lane >> 5;
   float* part = a.part + ((((size_t)n * a.Hk + kvh) * a.nsplit + split) * G) * (kAD + 2);
   if (kb >= len) {
@@ -499,19 +505,37 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   float mrun = -INFINITY, lsum = 0.f;
   const uint16_t* kbase = a.k_cache + ((size_t)n * a.cache_len * a.Hk + kvh) * kAD + 8 * hf;
   const uint16_t* vbase = a.v_cache + ((size_t)n * a.Hk + kvh) * kAD * a.cache_len + 8 * hf;
-  const int kend = min(kb + kDecSplit, len);
+  const int kend = min(kb + a.split_keys, len);
   for (int k0 = kb; k0 < kend; k0 += kKB) {
+    // all 32 K fragments of the block in flight at once (32 KiB per wave),
+    // then the MFMAs; scheduling barriers keep the loads from being sunk
+    // next to their uses
+    bf16x8 kf[32];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* krow = kbase + (size_t)(k0 + 32 * t + col) * a.Hk * kAD;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) kf[16 * t + ks] = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
-      const uint16_t* krow = kbase + (size_t)(k0 + 32 * t + col) * a.Hk * kAD;
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks)
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(krow + 16 * ks), qf[ks], s[t],
-                                                       0, 0, 0);
+        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[16 * t + ks], qf[ks], s[t], 0, 0, 0);
     }
+    // the block's V^T fragments go out before the softmax
+    bf16x8 vf[32];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint16_t* vrow = vbase + (size_t)(32 * dt + col) * a.cache_len + k0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) vf[4 * dt + g] = *reinterpret_cast<const bf16x8*>(vrow + 16 * g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float bmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -554,13 +578,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       pf[g] = __builtin_bit_cast(bf16x8, nat);
     }
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint16_t* vrow = vbase + (size_t)(32 * dt + col) * a.cache_len + k0;
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(vrow + 16 * g), pf[g], o[dt],
-                                                        0, 0, 0);
-    }
+      for (int g = 0; g < 4; ++g) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 * dt + g], pf[g], o[dt], 0, 0, 0);
   }
   lsum += __shfl_xor(lsum, 32, 64);
   if (col < G) {
@@ -582,10 +602,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s * sigmoid(gate).
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part, const uint16_t* gate,
                                                            const int32_t* cache_lens, uint16_t* out, int Hq, int Hk,
-                                                           int nsplit) {
+                                                           int nsplit, int split_keys) {
   const int n = blockIdx.x / Hq, h = blockIdx.x % Hq, d = threadIdx.x;
   const int G = Hq / Hk, kvh = h / G, c = h % G;
-  const int used = (cache_lens[n] + 1 + kDecSplit - 1) / kDecSplit;
+  const int used = (cache_lens[n] + 1 + split_keys - 1) / split_keys;
   const float* p = part + (((size_t)n * Hk + kvh) * nsplit * G + c) * (kAD + 2);
   const size_t stride = (size_t)G * (kAD + 2);
   float M = -INFINITY;
@@ -604,14 +624,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part, co
 }  // namespace
 
 size_t attn_decode_workspace_bytes(const AttnArgs& a) {
-  const size_t nsplit = (a.cache_len + kDecSplit - 1) / kDecSplit;
+  const int sk = dec_split_keys(a.N, a.Hk, a.cache_len);
+  const size_t nsplit = (a.cache_len + sk - 1) / sk;
   const size_t q = ((size_t)a.N * a.Hq * kAD * 2 + 255) / 256 * 256;
   return q + (size_t)a.N * a.Hk * nsplit * (a.Hq / a.Hk) * (kAD + 2) * 4;
 }
 
 hipError_t launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st) {
   if (a.N == 0) return hipSuccess;
-  const int nsplit = (a.cache_len + kDecSplit - 1) / kDecSplit;
+  const int sk = dec_split_keys(a.N, a.Hk, a.cache_len);
+  const int nsplit = (a.cache_len + sk - 1) / sk;
   unsigned char* p = static_cast<unsigned char*>(ws);
   uint16_t* q_rot = reinterpret_cast<uint16_t*>(p);
   float* part = reinterpret_cast<float*>(p + ((size_t)a.N * a.Hq * kAD * 2 + 255) / 256 * 256);
@@ -644,12 +666,13 @@ hipError_t launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st) {
   d.Hk = a.Hk;
   d.cache_len = a.cache_len;
   d.nsplit = nsplit;
+  d.split_keys = sk;
   d.scale_log2 = 1.4426950408889634f / 16.f;
   const int64_t waves = (int64_t)a.N * a.Hk * nsplit;
   hipLaunchKernelGGL(attn_decode_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, d);
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.N * a.Hq)), dim3(256), 0, st, part,
                      static_cast<const uint16_t*>(a.gate), a.cache_lens, static_cast<uint16_t*>(a.out), a.Hq, a.Hk,
-                     nsplit);
+                     nsplit, sk);
   return hipGetLastError();
 }
 
