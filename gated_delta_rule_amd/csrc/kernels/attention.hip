@@ -197,7 +197,9 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// V transposed per 64-key chunk: vt[h][d][64 c + slot] with keys in slot
+// V transposed per 64-key chunk into two 32-key tiles: vt[h][t][d][slot],
+// t = 2 c + slot / 32, each 256 x 32 tile contiguous (16 KiB, so one copy
+// instruction reads 1 KiB of it), keys in slot
 // order kPerm (within each group of 16 keys the middle two quarters swap),
 // the order in which the attention kernel's probabilities come out of its
 // score registers.  Keys past the sequence end are zero.
@@ -226,13 +228,14 @@ __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* v, const i
   uint16_t row[kKB];
 #pragma unroll
   for (int s = 0; s < kKB; ++s) row[s] = tile[(s & ~15) | kperm(s & 15)][d];
-  uint16_t* dst = vt + ((size_t)h * kAD + d) * tpad + (size_t)kKB * c;
 #pragma unroll
   for (int s = 0; s < kKB; s += 8) {
     u16x8 pk;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pk[e] = row[s + e];
-    *reinterpret_cast<u16x8*>(dst + s) = pk;
+    // 32-key tile 2c + s / 32, row d
+    uint16_t* dst = vt + (((size_t)h * (tpad / 32) + 2 * c + s / 32) * kAD + d) * 32 + s % 32;
+    *reinterpret_cast<u16x8*>(dst) = pk;
   }
   if (v_cache) {
     // [N, Hk, D, cache_len]: this chunk's keys k0 .. k0+63 of row d, natural
@@ -255,18 +258,21 @@ __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* v, const i
 
 // ---------------------------------------------------------------------------
 // Causal attention.  Workgroup: one query head, 128 queries of one sequence,
-// 4 waves of 32 queries.  Per 64-key block, staged in LDS (two stages of a
-// K tile [64 keys][256] and a V^T tile [256 dims][64 keys]):
-//   S^T = K Q^T   16 x 2 MFMAs (32x32x16): lane l holds query l % 32 and 16
-//                 of the block's keys per 32-key tile, so its softmax row
-//                 is in registers (the other 32 keys are in lane l ^ 32)
-//   online softmax in base 2 with a running maximum per query; the
-//                 accumulator is rescaled only when the maximum grows by more
-//                 than 8 (probabilities stay below 2^8)
-//   O^T += V^T P^T  8 dim tiles x 4 key steps: P comes straight from the
-//                 score registers (bf16), V^T from LDS
-// LDS swizzles put the 16 lanes of one 16-byte read on 16 bank groups:
-// K rows (512 B) use chunk c ^ (row & 15), V^T rows (128 B) c ^ ((row >> 1) & 7).
+// 4 waves of 32 queries.  Keys go in blocks of 32 through four LDS stages
+// (K tile [32 keys][256], V^T tile [256 dims][32 keys], 16 KiB each), copied
+// by direct-to-LDS loads three blocks ahead of their use.  Per block j, one
+// wave does
+//   S^T(j+1) = K Q^T   16 MFMAs (32x32x16): lane l holds query l % 32 and 16
+//                      of the block's keys (the other 16 are in lane l ^ 32)
+//   softmax(j)         online, base 2, on the scores of the previous
+//                      iteration, so its VALU work runs beside the MFMAs of
+//                      S(j+1); the accumulator is rescaled only when the
+//                      running maximum grows by more than 8
+//   O^T += V^T P^T(j)  8 dim tiles x 2 key steps, P straight from the score
+//                      registers (bf16)
+// with the block's eight copy pieces spread between the MFMAs.  LDS swizzles
+// put the 16 lanes of one 16-byte read on 16 bank groups: K rows (512 B) use
+// chunk c ^ (row & 15), V^T rows (64 B) c ^ ((row >> 2) & 3).
 struct FwdArgs {
   const uint16_t *q_rot, *k_pad, *vt, *gate;
   const int32_t *cu, *table;
@@ -277,13 +283,17 @@ struct FwdArgs {
 };
 
 constexpr float kRescale = 8.f;
+constexpr int kFB = 32;    // keys per block
+constexpr int kStg = 4;    // LDS stages
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t* s, int row, int pitch_chunks, int chunk) {
   return *reinterpret_cast<const bf16x8*>(s + row * pitch_chunks * 8 + 8 * chunk);
 }
+__device__ __forceinline__ void wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+__device__ __forceinline__ void wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
 
 __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
-  __shared__ __align__(16) uint16_t sK[2][kKB * kAD], sV[2][kAD * kKB];
+  __shared__ __align__(16) uint16_t sK[kStg][kFB * kAD], sV[kStg][kAD * kFB];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = a.Hq / a.Hk;
@@ -304,8 +314,9 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
   const int qw = q0 + 32 * wave;                       // first query of this wave
   const int my_q = min(qw + (lane & 31), L - 1);       // this lane's query (rows past L repeat the last)
   const int last_q = min(q0 + kQB - 1, L - 1);
-  const int nkb = last_q / kKB + 1;
+  const int nkb = last_q / kFB + 1;
   const int64_t kp0 = (int64_t)kKB * a.table[n];       // first padded key of the sequence
+  const int64_t vt0 = (int64_t)kvh * (a.tpad / kFB) + kp0 / kFB;  // its first V^T tile
 
   // Q^T fragments (B operand): query my_q, dims 16 ks + 8 (l / 32) .. +7
   bf16x8 qf[16];
@@ -322,62 +333,70 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
     for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
   float mrun = -INFINITY, lsum = 0.f;
 
-  // copy of key block j into stage st: this wave's 8 K pieces (2 rows each)
-  // and 8 V^T pieces (8 rows each)
-  auto copy_piece = [&](int j, int st, int i) {
-    if (i < 8) {
-      const int row = 16 * wave + 2 * i + (lane >> 5);
+  // piece i (0..7) of the copy of key block jb (clamped to the last block,
+  // so every iteration issues eight) into stage jb % 4: pieces 0..3 are K
+  // rows 8 wave + 2 i .. +1, pieces 4..7 V^T rows 64 wave + 16 (i - 4) .. +15
+  auto copy_piece = [&](int jb, int i) {
+    const int st = jb % kStg;
+    jb = min(jb, nkb - 1);
+    if (i < 4) {
+      const int rb = 8 * wave + 2 * i, row = rb + (lane >> 5);
       const int c = (lane & 31) ^ (row & 15);
-      const uint16_t* g = a.k_pad + ((kp0 + (int64_t)kKB * j + row) * a.Hk + kvh) * kAD + 8 * c;
-      dma16(g, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)(sK[st] + (16 * wave + 2 * i) * kAD)));
+      const uint16_t* g = a.k_pad + ((kp0 + (int64_t)kFB * jb + row) * a.Hk + kvh) * kAD + 8 * c;
+      dma16(g, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)(sK[st] + rb * kAD)));
     } else {
-      const int r0 = 64 * wave + 8 * (i - 8), row = r0 + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
-      const uint16_t* g = a.vt + ((int64_t)kvh * kAD + row) * a.tpad + kp0 + (int64_t)kKB * j + 8 * c;
-      dma16(g, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)(sV[st] + r0 * kKB)));
+      const int r0 = 64 * wave + 16 * (i - 4), row = r0 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const uint16_t* g = a.vt + ((vt0 + jb) * kAD + row) * kFB + 8 * c;
+      dma16(g, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)(sV[st] + r0 * kFB)));
+    }
+  };
+  // scores of block jb: K fragments read two key steps ahead of their MFMAs
+  auto scores = [&](int jb, f32x16& s) {
+    const uint16_t* K = sK[jb % kStg];
+    const int row = lane & 31;
+    auto kfrag = [&](int ks) { return lds_frag(K, row, kAD / 8, (2 * ks + (lane >> 5)) ^ (row & 15)); };
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[e] = 0.f;
+    bf16x8 kr[3];
+    kr[0] = kfrag(0);
+    kr[1] = kfrag(1);
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      if (ks + 2 < 16) kr[(ks + 2) % 3] = kfrag(ks + 2);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[ks % 3], qf[ks], s, 0, 0, 0);
     }
   };
 
 #pragma unroll
-  for (int i = 0; i < 16; ++i) copy_piece(0, 0, i);
+  for (int jb = 0; jb < kStg - 1; ++jb)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) copy_piece(jb, i);
+  wait_vm16();
+  __syncthreads();
+  f32x16 sc;
+  scores(0, sc);
 
   for (int j = 0; j < nkb; ++j) {
-    const int st = j & 1;
-    const bool next = j + 1 < nkb;
-    wait_vm0();
-    __syncthreads();
-    const uint16_t* K = sK[st];
-    const uint16_t* V = sV[st];
-    // S^T = K Q^T for the two 32-key tiles; the next block's copy goes out
-    // between these MFMAs
-    f32x16 s[2];
+    wait_vm8();      // this wave's copy of block j+1 has landed (j+2 may be in flight)
+    __syncthreads(); // ... and every wave's; every wave is done with block j-1's stage
+    // (unconditional, so the scheduler can interleave these MFMAs with the
+    // softmax below; after the last block it scores a clamped block that is
+    // never used)
+    f32x16 sn;
+    scores(min(j + 1, nkb - 1), sn);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int row = 32 * t + (lane & 31);
-        const int c = (2 * ks + (lane >> 5)) ^ (row & 15);
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(K, row, kAD / 8, c), qf[ks], s[t], 0, 0, 0);
-      }
-      if (next) copy_piece(j + 1, st ^ 1, ks);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // mask and online softmax (base 2)
-    const int kb0 = kKB * j;
+    for (int i = 0; i < 4; ++i) copy_piece(j + kStg - 1, i);
+    // mask and online softmax (base 2) of block j
+    const int kb0 = kFB * j;
     float bmax = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb0 + 32 * t + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const float v = key <= my_q ? s[t][r] * a.scale_log2 : -INFINITY;
-        s[t][r] = v;
-        bmax = fmaxf(bmax, v);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int key = kb0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const float v = key <= my_q ? sc[r] * a.scale_log2 : -INFINITY;
+      sc[r] = v;
+      bmax = fmaxf(bmax, v);
+    }
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
     const bool grow = bmax > mrun + kRescale;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -390,30 +409,32 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
         for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
       mrun = mnew;
     }
-    bf16x8 pf[2][2];
+    bf16x8 pf[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int uu = 0; uu < 2; ++uu) {
+      u16x8 pk;
 #pragma unroll
-      for (int uu = 0; uu < 2; ++uu) {
-        u16x8 pk;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(s[t][8 * uu + e] - mrun);
-          lsum += p;
-          pk[e] = f32_to_bf16(p);
-        }
-        pf[t][uu] = __builtin_bit_cast(bf16x8, pk);
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(sc[8 * uu + e] - mrun);
+        lsum += p;
+        pk[e] = f32_to_bf16(p);
       }
-    // O^T += V^T P^T: 8 dim tiles, 4 steps of 16 keys (tile t, half uu)
+      pf[uu] = __builtin_bit_cast(bf16x8, pk);
+    }
+    // O^T += V^T P^T: 8 dim tiles, 2 steps of 16 keys; the other half of
+    // the copy goes out between them
+    const uint16_t* V = sV[j % kStg];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const int row = 32 * dt + (lane & 31);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = (2 * g + (lane >> 5)) ^ ((row >> 1) & 7);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(V, row, kKB / 8, c), pf[g >> 1][g & 1], o[dt], 0, 0, 0);
+      for (int g = 0; g < 2; ++g) {
+        const int c = (2 * g + (lane >> 5)) ^ ((row >> 2) & 3);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(V, row, kFB / 8, c), pf[g], o[dt], 0, 0, 0);
       }
+      if (dt & 1) copy_piece(j + kStg - 1, 4 + (dt >> 1));
     }
+    sc = sn;
   }
   wait_vm0();
 
