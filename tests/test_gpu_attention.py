@@ -222,3 +222,44 @@ def test_decode_full_size_sampled():
         vn = to_host(vc[n:n + 1, :, :, :p + 1]).transpose(0, 3, 1, 2)
         r = aref.core_decode(to_host(qg)[None], x.gate[n:n + 1], kn, vn, np.array([p + 1]))
         _check_out(to_host(out[n:n + 1]), r["out"], r["mass"])
+
+
+def test_prefill_many_short_sequences():
+    """300 sequences of 0 .. 70 tokens (more sequences than the offset
+    table's threads, many of them empty or single-token)."""
+    import gated_delta_rule_amd as gdr
+    import torch
+    dev = gpu()
+    lens = [int(x) for x in synth.rng(53).integers(0, 71, size=300)]
+    lens[7] = 0
+    lens[8] = 1
+    x = synth.attn_inputs(54, lengths=lens, hq=8, hk=2)
+    say("attention prefill 300 short sequences")
+    q, k, v, g, qw, kw, cu = _dev(x, dev)
+    out = gdr.attn_prefill(q, k, v, g, qw, kw, cu)
+    qo, ko = gdr.attn_qk_norm_rope(q, k, qw, kw, cu)
+    torch.cuda.synchronize()
+    r = aref.core_prefill(to_host(qo), to_host(ko), x.v, x.gate, x.cu_seqlens)
+    _check_out(to_host(out), r["out"], r["mass"])
+
+
+def test_decode_full_cache():
+    """A token at the cache's last slot attends to every cached position;
+    one at slot 0 to itself only."""
+    import gated_delta_rule_amd as gdr
+    import torch
+    dev = gpu()
+    N, L, hq, hk = 2, 320, 24, 4
+    lens = (L - 1, 0)
+    x = synth.attn_inputs(55, lengths=(1,) * N, hq=hq, hk=hk)
+    rng = synth.rng(56)
+    kc0 = synth.round_bf16(rng.standard_normal((N, L, hk, 256)))
+    vc0 = synth.round_bf16(rng.standard_normal((N, hk, 256, L)))
+    say("attention decode at the last cache slot")
+    q, k, v, g, qw, kw, _ = _dev(x, dev)
+    kc, vc = to_dev(kc0, "bf16", dev), to_dev(vc0, "bf16", dev)
+    out = gdr.attn_decode(q, k, v, g, qw, kw, kc, vc, torch.tensor(lens, device=dev, dtype=torch.int32))
+    torch.cuda.synchronize()
+    qrot = np.stack([to_host(_gpu_qrot_at(q[n], k[n], qw, kw, p, dev)[0]) for n, p in enumerate(lens)])
+    r = aref.core_decode(qrot, x.gate, to_host(kc), to_host(vc).transpose(0, 3, 1, 2), np.asarray(lens) + 1)
+    _check_out(to_host(out), r["out"], r["mass"])
