@@ -463,22 +463,30 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // Decode: one query token per sequence against its cache.  Each wave takes
-// one split (256 .. 2048 keys) of one (sequence, kv head) and the G query heads that
-// read it, with no LDS: its MFMA operands come straight from the caches
-// (K [N, L, Hk, D] rows, V^T [N, Hk, D, L] rows, both 16 bytes per lane).
-//   S^T = K Q^T   query columns = the G heads (the other lanes' columns are
-//                 zero), 32-key tiles as in the prefill
-//   softmax as in the prefill; the probabilities are put back in natural key
-//   order with two lane exchanges per 16 keys (the prefill instead permutes
-//   its V^T copy)
-//   O^T += V^T P^T
-// The split's running maximum, sum and unnormalised output go to a
-// workspace; attn_combine_kernel merges the splits and applies the gate.
+// one split (256 .. 2048 keys) of one (sequence, kv head) and the G query
+// heads that read it, with no LDS: its MFMA operands come straight from the
+// caches (K [N, L, Hk, D] rows, V^T [N, Hk, D, L] rows).  16x16x32 MFMAs keep
+// the heads in 16 columns (the other columns' queries are zero), so a wave
+// needs about half the registers of 32-wide tiles and two waves share a
+// SIMD.  Per 32-key block:
+//   S^T = K Q^T   2 key tiles x 8 dim steps; lane l holds head l % 16 and
+//                 keys 16 t + 4 (l / 16) + i of tile t
+//   softmax as in the prefill, over the 4 lane groups of each head
+//   O^T += V^T P^T  16 dim tiles, one 32-key step; lane group g supplies
+//                 the keys it holds, {4 g .. 4 g + 3, 16 + 4 g .. +3}, and reads
+//                 the same keys of V^T (two 8-byte loads)
+// All of a block's K loads go out before its MFMAs and all of its V loads
+// before the softmax (scheduling barriers keep them from being sunk next to
+// their uses).  The split's running maximum, sum and unnormalised output go
+// to a workspace; attn_combine_kernel merges the splits and applies the gate.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
 // Keys per split: 256 .. 2048 (a multiple of 64), chosen on the host so that
-// a step has about 4096 waves.
+// a step has about 8192 waves.
 __host__ __device__ inline int dec_split_keys(int N, int Hk, int cache_len) {
   int s = 256;
-  while (s < 2048 && (int64_t)N * Hk * ((cache_len + 2 * s - 1) / (2 * s)) >= 4096) s *= 2;
+  while (s < 2048 && (int64_t)N * Hk * ((cache_len + 2 * s - 1) / (2 * s)) >= 8192) s *= 2;
   return s;
 }
 
@@ -491,7 +499,7 @@ struct DecArgs {
   float scale_log2;
 };
 
-__global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecArgs a) {
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int split = gw % a.nsplit, nk = gw / a.nsplit;
@@ -500,73 +508,68 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
   const int G = a.Hq / a.Hk;
   const int len = a.cache_lens[n] + 1;
   const int kb = split * a.split_keys;
-  const int col = lane & 31, hf = lane >> 5;
+  const int col = lane & 15, grp = lane >> 4;
   float* part = a.part + ((((size_t)n * a.Hk + kvh) * a.nsplit + split) * G) * (kAD + 2);
   if (kb >= len) {
-    if (col < G && hf == 0) {
+    if (col < G && grp == 0) {
       part[col * (kAD + 2) + kAD] = -INFINITY;
       part[col * (kAD + 2) + kAD + 1] = 0.f;
     }
     return;
   }
-  bf16x8 qf[16];
+  // Q^T fragments (B operand): head col, dims 32 ks + 8 grp .. +7
+  bf16x8 qf[8];
   {
-    const uint16_t* qrow = a.q_rot + ((size_t)n * a.Hq + kvh * G + min(col, G - 1)) * kAD + 8 * hf;
+    const uint16_t* qrow = a.q_rot + ((size_t)n * a.Hq + kvh * G + min(col, G - 1)) * kAD + 8 * grp;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks);
+    for (int ks = 0; ks < 8; ++ks) {
+      qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
       if (col >= G) qf[ks] = bf16x8{};
     }
   }
-  f32x16 o[8];
+  f32x4v o[16];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+  for (int i = 0; i < 16; ++i) o[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lsum = 0.f;
-  const uint16_t* kbase = a.k_cache + ((size_t)n * a.cache_len * a.Hk + kvh) * kAD + 8 * hf;
-  const uint16_t* vbase = a.v_cache + ((size_t)n * a.Hk + kvh) * kAD * a.cache_len + 8 * hf;
+  const uint16_t* kbase = a.k_cache + ((size_t)n * a.cache_len * a.Hk + kvh) * kAD + 8 * grp;
+  const uint16_t* vbase = a.v_cache + ((size_t)n * a.Hk + kvh) * kAD * a.cache_len + 4 * grp;
   const int kend = min(kb + a.split_keys, len);
-  for (int k0 = kb; k0 < kend; k0 += kKB) {
-    // all 32 K fragments of the block in flight at once (32 KiB per wave),
-    // then the MFMAs; scheduling barriers keep the loads from being sunk
-    // next to their uses
-    bf16x8 kf[32];
+  for (int k0 = kb; k0 < kend; k0 += 32) {
+    bf16x8 kf[16];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint16_t* krow = kbase + (size_t)(k0 + 32 * t + col) * a.Hk * kAD;
+      const uint16_t* krow = kbase + (size_t)(k0 + 16 * t + col) * a.Hk * kAD;
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) kf[16 * t + ks] = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
+      for (int ks = 0; ks < 8; ++ks) kf[8 * t + ks] = *reinterpret_cast<const bf16x8*>(krow + 32 * ks);
     }
     __builtin_amdgcn_sched_barrier(0);
-    f32x16 s[2];
+    f32x4v s[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      s[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks)
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[16 * t + ks], qf[ks], s[t], 0, 0, 0);
+      for (int ks = 0; ks < 8; ++ks) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[8 * t + ks], qf[ks], s[t], 0, 0, 0);
     }
-    // the block's V^T fragments go out before the softmax
-    bf16x8 vf[32];
+    // V^T fragments: dim row 16 dt + col, keys 4 grp .. +3 and 16 + 4 grp .. +3
+    u32x2v vf[16][2];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const uint16_t* vrow = vbase + (size_t)(32 * dt + col) * a.cache_len + k0;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) vf[4 * dt + g] = *reinterpret_cast<const bf16x8*>(vrow + 16 * g);
+    for (int dt = 0; dt < 16; ++dt) {
+      const uint16_t* vrow = vbase + (size_t)(16 * dt + col) * a.cache_len + k0;
+      vf[dt][0] = *reinterpret_cast<const u32x2v*>(vrow);
+      vf[dt][1] = *reinterpret_cast<const u32x2v*>(vrow + 16);
     }
     __builtin_amdgcn_sched_barrier(0);
     float bmax = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-        const float v = key < len ? s[t][r] * a.scale_log2 : -INFINITY;
-        s[t][r] = v;
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + 16 * t + 4 * grp + i;
+        const float v = key < len ? s[t][i] * a.scale_log2 : -INFINITY;
+        s[t][i] = v;
         bmax = fmaxf(bmax, v);
       }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
     const bool grow = bmax > mrun + kRescale;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -574,45 +577,33 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(DecArgs a) {
       const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
       lsum *= alpha;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+      for (int i = 0; i < 16; ++i) o[i] *= alpha;
       mrun = mnew;
     }
-    // probabilities, then natural key order: lane half hf holds keys
-    // {4 hf .. 4 hf + 3, 8 + 4 hf .. 8 + 4 hf + 3} of each 16; after the
-    // exchange it holds 8 hf .. 8 hf + 7
-    bf16x8 pf[4];
+    uint32_t pk[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      uint32_t d[4];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + 2 * e] - mrun);
-        const float p1 = __builtin_amdgcn_exp2f(s[g >> 1][8 * (g & 1) + 2 * e + 1] - mrun);
+      for (int e = 0; e < 2; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(s[t][2 * e] - mrun);
+        const float p1 = __builtin_amdgcn_exp2f(s[t][2 * e + 1] - mrun);
         lsum += p0 + p1;
-        d[e] = pack_bf16x2(p0, p1);
+        pk[2 * t + e] = pack_bf16x2(p0, p1);
       }
-      const uint32_t x0 = __shfl_xor(hf ? d[0] : d[2], 32, 64);
-      const uint32_t x1 = __shfl_xor(hf ? d[1] : d[3], 32, 64);
-      const u32x4 nat = hf ? u32x4{x0, x1, d[2], d[3]} : u32x4{d[0], d[1], x0, x1};
-      pf[g] = __builtin_bit_cast(bf16x8, nat);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      const bf16x8 af = __builtin_bit_cast(bf16x8, u32x4{vf[dt][0][0], vf[dt][0][1], vf[dt][1][0], vf[dt][1][1]});
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, o[dt], 0, 0, 0);
     }
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[4 * dt + g], pf[g], o[dt], 0, 0, 0);
   }
+  lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
   if (col < G) {
     float* pr = part + col * (kAD + 2);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4)
-        *reinterpret_cast<f32x4*>(pr + 32 * dt + 8 * g4 + 4 * hf) =
-            f32x4{o[dt][4 * g4], o[dt][4 * g4 + 1], o[dt][4 * g4 + 2], o[dt][4 * g4 + 3]};
-    if (hf == 0) {
+    for (int dt = 0; dt < 16; ++dt) *reinterpret_cast<f32x4*>(pr + 16 * dt + 4 * grp) = o[dt];
+    if (grp == 0) {
       pr[kAD] = mrun;
       pr[kAD + 1] = lsum;
     }
