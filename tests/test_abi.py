@@ -226,6 +226,51 @@ def test_delta_layer_validation_and_workspace():
     assert lib.gdr_delta_layer_fwd(None, *([FAKE] * 14), 1 << 40, None) == -1
 
 
+def _attn_desc(T=64, N=1, hq=24, hk=4, d=256, L=0):
+    a = _lib.GdrAttnDesc()
+    a.struct_size = ctypes.sizeof(_lib.GdrAttnDesc)
+    a.num_tokens, a.num_seqs, a.num_q_heads, a.num_kv_heads, a.head_dim = T, N, hq, hk, d
+    a.cache_len, a.norm_eps, a.rope_base = L, 1e-6, 1e7
+    return a
+
+
+def test_attention_validation_and_workspace():
+    lib = _lib.load()
+    n = ctypes.c_size_t(0)
+    d = _attn_desc(T=32768)
+    assert lib.gdr_attn_prefill_workspace_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    q_rot = 32768 * 24 * 256 * 2
+    assert q_rot < n.value < q_rot + 2 * (32768 + 128) * 4 * 256 * 2 + 4096
+    assert lib.gdr_attn_prefill_workspace_size(ctypes.byref(_attn_desc(d=128)), ctypes.byref(n)) == -2
+    assert lib.gdr_attn_prefill_workspace_size(ctypes.byref(_attn_desc(hq=10)), ctypes.byref(n)) == -2
+    assert lib.gdr_attn_prefill_workspace_size(ctypes.byref(_attn_desc(N=0)), ctypes.byref(n)) == -1
+    P = [FAKE] * 11
+    d = _attn_desc()
+    assert lib.gdr_attn_prefill(ctypes.byref(d), *P, 16, None) == -1  # short workspace
+    args = list(P)
+    args[9] = None  # k_cache without v_cache
+    assert lib.gdr_attn_prefill(ctypes.byref(d), *args, 1 << 40, None) == -1
+    assert "both" in lib.gdr_last_error().decode()
+    d = _attn_desc(L=100)  # cache_len not a multiple of 64
+    assert lib.gdr_attn_prefill(ctypes.byref(d), *P, 1 << 40, None) == -1
+    args = list(P)
+    args[6] = None  # no cu_seqlens
+    assert lib.gdr_attn_prefill(ctypes.byref(_attn_desc()), *args, 1 << 40, None) == -1
+    # decode
+    dd = _attn_desc(T=64, N=64, L=32768)
+    assert lib.gdr_attn_decode_workspace_size(ctypes.byref(dd), ctypes.byref(n)) == 0
+    assert n.value >= 64 * 24 * 256 * 2
+    assert lib.gdr_attn_decode_workspace_size(ctypes.byref(_attn_desc(T=64, N=64, L=0)), ctypes.byref(n)) == -1
+    assert lib.gdr_attn_decode_workspace_size(ctypes.byref(_attn_desc(T=3, N=64, L=64)), ctypes.byref(n)) == -1
+    assert lib.gdr_attn_decode(ctypes.byref(dd), *P, 16, None) == -1  # short workspace
+    args = list(P)
+    args[8] = None  # no cache_lens
+    assert lib.gdr_attn_decode(ctypes.byref(dd), *args, 1 << 40, None) == -1
+    assert lib.gdr_attn_decode(ctypes.byref(dd), *[FAKE + 8] + P[1:], 1 << 40, None) == -1  # misaligned q
+    assert lib.gdr_attn_qk_norm_rope(ctypes.byref(_attn_desc()), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                                     None) == -1
+
+
 def test_no_oracle_in_product_path():
     """The library and its binding never import the oracle."""
     pkg = os.path.join(ROOT, "gated_delta_rule_amd")
