@@ -10,9 +10,10 @@
 // reads -- the key head's q and k channels and its value heads' v channels --
 // so it updates their conv state in place without racing another workgroup.
 //
-//   phase 0  every lane issues its 16 state loads (non-temporal), as in the
-//            decode kernel: waves 4g .. 4g+3 stream value head kh*G + g,
-//            32 rows each, 8 lanes per row
+//   phase 0  each thread loads its conv channel's inputs and (threads
+//            0 .. G-1) the gate inputs, then every lane issues its 16 state
+//            loads (non-temporal), as in the decode kernel: waves 4g .. 4g+3
+//            stream value head kh*G + g, 32 rows each, 8 lanes per row
 //   phase 1  conv + SiLU of the (2 + G) * 128 channels under the front's
 //            bit-exact contract (same code as the prefill front), the
 //            conv state rolled by one token, the gates; results to LDS
@@ -70,7 +71,30 @@ __global__ __launch_bounds__(256 * G) void decode_layer_kernel(LayerStepArgs a) 
     return;
   }
 
-  // ---- phase 0: state loads
+  // ---- phase 0: this thread's conv channel inputs, then the state loads.
+  // Loads complete in issue order, so the small conv loads go first: the
+  // conv, its LDS writes and the barrier then run while the state streams in.
+  constexpr int NCH = (2 + G) * D, CPT = (NCH + 256 * G - 1) / (256 * G);  // conv channels per thread
+  const uint16_t* x = static_cast<const uint16_t*>(a.x) + (size_t)n * C;
+  const uint16_t* w = static_cast<const uint16_t*>(a.conv_w);
+  uint16_t* cst = static_cast<uint16_t*>(a.conv_state) + (size_t)slot * C * 3;
+  uint16_t xr[CPT], h0[CPT], h1[CPT], h2[CPT];
+  u16x4 wr[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    // unconditional (clamped) loads: a branch here would let the compiler
+    // consume them, and so wait for them, before the state loads issue
+    const int c = channel(min(tid + 256 * G * i, NCH - 1));
+    const uint16_t* cs = cst + (size_t)c * 3;
+    xr[i] = x[c];
+    wr[i] = *reinterpret_cast<const u16x4*>(w + (size_t)c * 4);
+    h0[i] = cs[0];
+    h1[i] = cs[1];
+    h2[i] = cs[2];
+  }
+  const int gh_ld = kh * G + min(tid, G - 1);
+  const float ga = a.a[(size_t)n * a.Hv + gh_ld], gb = a.b[(size_t)n * a.Hv + gh_ld];
+  const float gA = a.A_log[gh_ld], gdt = a.dt_bias[gh_ld];
   const int row0 = wh * (D / 4) + sub;
   float* S = a.state + ((size_t)slot * a.Hv + h) * D * D;
   f32x4 s[NS][F4];
@@ -79,33 +103,29 @@ __global__ __launch_bounds__(256 * G) void decode_layer_kernel(LayerStepArgs a) 
 #pragma unroll
     for (int j = 0; j < F4; ++j)
       s[i][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(row0 + 8 * i) * D + 32 * j + 4 * e8));
+  __builtin_amdgcn_sched_barrier(0);  // every load above issues before any use
 
   // ---- phase 1: conv + SiLU, rolling conv state, gates
   {
-    const uint16_t* x = static_cast<const uint16_t*>(a.x) + (size_t)n * C;
-    const uint16_t* w = static_cast<const uint16_t*>(a.conv_w);
-    uint16_t* cst = static_cast<uint16_t*>(a.conv_state) + (size_t)slot * C * 3;
-    for (int cl = tid; cl < (2 + G) * D; cl += 256 * G) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int cl = tid + 256 * G * i;
+      if (cl >= NCH) continue;
       const int c = channel(cl);
-      const uint16_t xr = x[c];
-      const u16x4 wr = *reinterpret_cast<const u16x4*>(w + (size_t)c * 4);
-      uint16_t* cs = cst + (size_t)c * 3;
-      const uint16_t h0 = cs[0], h1 = cs[1], h2 = cs[2];
-      const float acc = conv4(bf16_to_f32(wr[0]), bf16_to_f32(wr[1]), bf16_to_f32(wr[2]), bf16_to_f32(wr[3]),
-                              bf16_to_f32(h0), bf16_to_f32(h1), bf16_to_f32(h2), bf16_to_f32(xr));
+      const float acc = conv4(bf16_to_f32(wr[i][0]), bf16_to_f32(wr[i][1]), bf16_to_f32(wr[i][2]),
+                              bf16_to_f32(wr[i][3]), bf16_to_f32(h0[i]), bf16_to_f32(h1[i]), bf16_to_f32(h2[i]),
+                              bf16_to_f32(xr[i]));
       // same bits on either path; the wave takes the short one when it can
       const float yv = __all(fabsf(acc) <= 80.f) ? silu32_mid(acc) : silu32(acc);
       const uint16_t yb = f32_to_bf16(yv);
       xs[cl] = bf16_to_f32(yb);
       if (a.qkv_out) static_cast<uint16_t*>(a.qkv_out)[(size_t)n * C + c] = yb;
-      cs[0] = h1;
-      cs[1] = h2;
-      cs[2] = xr;
+      uint16_t* cs = cst + (size_t)c * 3;
+      cs[0] = h1[i];
+      cs[1] = h2[i];
+      cs[2] = xr[i];
     }
-    if (tid < G) {
-      const int hh = kh * G + tid;
-      gates(a.a[(size_t)n * a.Hv + hh], a.b[(size_t)n * a.Hv + hh], a.A_log[hh], a.dt_bias[hh], gl[tid], bl[tid]);
-    }
+    if (tid < G) gates(ga, gb, gA, gdt, gl[tid], bl[tid]);
   }
   lds_sync();
 
