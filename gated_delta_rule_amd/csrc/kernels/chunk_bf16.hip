@@ -503,13 +503,16 @@ __global__ __launch_bounds__(kNT, 4) void chunk_prep_kernel(ChunkArgs a, unsigne
 //                     O = yq * (Q S0^T) + P Delta off the chain;
 //   load waves 4, 5   fetch each chunk's inputs into registers two chunks
 //                     ahead and write them to LDS one chunk ahead.
-// So the state waves never issue a global load or store.
+// So the state waves never issue a global load or store.  Waves go to the
+// four SIMDs in turn, so each state wave shares its SIMD with a load wave,
+// which waits at barriers most of the time, rather than with a busy output
+// wave.
 
 constexpr int kRecNT = 384;  // threads per recurrence workgroup: 2 state + 2 output + 2 load waves
 
 // One chunk's shared inputs in LDS (62 KiB; two buffers).  Every region is a
-// whole number of 1 KiB blocks, so one 64-lane direct-to-LDS load (16 bytes
-// per lane) fills one block:
+// whole number of 1 KiB blocks, so one 64-lane load of 16 bytes per lane
+// fills one block:
 //   K, Q (16 blocks each): 64 rows x 256 bytes; 16-byte slot s of row r is
 //        kept at slot s ^ kqswz(r), which makes the row-strided fragment reads
 //        and the transposing reads of the state phase conflict-free
@@ -547,21 +550,19 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
-// Per-lane parts of the direct-load source offsets (bytes) of load wave lw.
+// Per-lane parts of the load source offsets (bytes) of load wave lw.
 struct RecLane {
-  uint32_t kq_e, kq_o;  // k/q block b: row 4b + lane/16, slot (lane%16) ^ kqswz(row); b%4 = lw, lw + 2
-  uint32_t slot0;       // (lane%16) ^ 4 (lane/16)
-  uint32_t lane16;      // 16 lane
-  uint32_t fac;         // factor blocks: 16 lane (lw 0), 16 min(lane, 7) (lw 1: e^{G_L} only)
-  uint32_t v;           // v block b: row 16b + lane/4, slot lane%4
+  uint32_t slot0;   // (lane%16) ^ 4 (lane/16): k/q block b reads slot slot0 ^ (b%4) of row 4b + lane/16
+  uint32_t lane16;  // 16 lane
+  uint32_t fac;     // factor blocks: 16 lane (lw 0), 16 min(lane, 7) (lw 1: e^{G_L} only)
 };
 
 // Source of load wave lw's block jj of one chunk (block i = lw + 2 jj, lane
 // `lane`).  kb, qb, vb point at row 0 of the chunk (k, q of the key head;
-// this workgroup's v channels), rb at the chunk record.  kFull: a whole
-// chunk; otherwise rows at or past L repeat row L-1 (they are never used,
-// but must be finite).
-template <bool kFull>
+// this workgroup's v channels), rb at the chunk record.  Rows at or past L
+// (a partial last chunk) repeat row L-1: they are never used, but must be
+// finite.  Whole and partial chunks take the same code, so the load waves'
+// loop has no branch around its loads.
 __device__ __forceinline__ const unsigned char* rec_src(int jj, const unsigned char* kb, const unsigned char* qb,
                                                         const unsigned char* rb, const unsigned char* vb,
                                                         const RecLane& ln, int lw, int lane, int row_bytes,
@@ -570,34 +571,32 @@ __device__ __forceinline__ const unsigned char* rec_src(int jj, const unsigned c
   if (2 * jj < kBlkM) {  // k or q: block b covers rows 4b .. 4b+3
     const int b = 2 * jj < kBlkQ ? i : i - kBlkQ;
     const unsigned char* base = 2 * jj < kBlkQ ? kb : qb;
-    if (kFull) return base + (size_t)(4 * b) * row_bytes + ((jj & 1) ? ln.kq_o : ln.kq_e);
     const int row = min(4 * b + (lane >> 4), L - 1);
     return base + (size_t)row * row_bytes + 16 * (ln.slot0 ^ (uint32_t)(b & 3));
   }
   if (2 * jj < kBlkF) return rb + 1024 * (i - kBlkM) + ln.lane16;
   if (2 * jj < kBlkV) return rb + kFacOff + 1024 * lw + ln.fac;
   const int b = i - kBlkV;
-  if (kFull) return vb + (size_t)(16 * b) * vrow_bytes + ln.v;
   const int row = min(16 * b + (lane >> 2), L - 1);
   return vb + (size_t)row * vrow_bytes + 16 * (lane & 3);
 }
 
-// Load wave lw's blocks jj0..jj1-1 of one chunk into registers, and from there into
-// an LDS buffer (each lane's 16 bytes of block i land at 1024 i + 16 lane).
-template <bool kFull>
+// Load wave lw's blocks jj0..jj1-1 of one chunk into registers (each lane's 16
+// bytes of block i go to LDS at 1024 i + 16 lane later, see rec_put).
 __device__ __forceinline__ void rec_fetch(u32x4* stage, const unsigned char* kb, const unsigned char* qb,
                                           const unsigned char* rb, const unsigned char* vb, const RecLane& ln,
                                           int lw, int lane, int row_bytes, int vrow_bytes, int L, int jj0, int jj1) {
 #pragma unroll
   for (int jj = 0; jj < kLoadsPerWave; ++jj)
     if (jj >= jj0 && jj < jj1)
-      stage[jj] = *reinterpret_cast<const u32x4*>(
-        rec_src<kFull>(jj, kb, qb, rb, vb, ln, lw, lane, row_bytes, vrow_bytes, L));
+      stage[jj] = *reinterpret_cast<const u32x4*>(rec_src(jj, kb, qb, rb, vb, ln, lw, lane, row_bytes, vrow_bytes, L));
 }
-__device__ __forceinline__ void rec_put(RecBuf* buf, const u32x4* stage, int lw, int lane) {
+__device__ __forceinline__ void rec_put(RecBuf* buf, const u32x4* stage, int lw, int lane, int jj0 = 0,
+                                        int jj1 = kLoadsPerWave) {
 #pragma unroll
   for (int jj = 0; jj < kLoadsPerWave; ++jj)
-    *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(buf) + 1024 * (lw + 2 * jj) + 16 * lane) = stage[jj];
+    if (jj >= jj0 && jj < jj1)
+      *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(buf) + 1024 * (lw + 2 * jj) + 16 * lane) = stage[jj];
 }
 
 // Output stores of tiles ti0..ti1-1 of one chunk: Ot[ti][i] is the output of
@@ -708,16 +707,9 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
   const int row_bytes = (int)(kqts * 2), vrow_bytes = (int)(vts * 2);
 
   RecLane ln;
-  {
-    const uint32_t s0 = (uint32_t)((lane & 15) ^ (4 * (lane >> 4)));
-    const uint32_t rb = (uint32_t)(lane >> 4) * row_bytes;
-    ln.slot0 = s0;
-    ln.kq_e = rb + 16 * (s0 ^ (uint32_t)wave);
-    ln.kq_o = rb + 16 * (s0 ^ (uint32_t)(wave + 2));
-    ln.lane16 = 16 * lane;
-    ln.fac = wave ? 16 * min(lane, 7) : 16 * lane;
-    ln.v = (uint32_t)(lane >> 2) * vrow_bytes + 16 * (lane & 3);
-  }
+  ln.slot0 = (uint32_t)((lane & 15) ^ (4 * (lane >> 4)));
+  ln.lane16 = 16 * lane;
+  ln.fac = wave ? 16 * min(lane, 7) : 16 * lane;
   // LDS byte offsets of this lane's fragment reads (see RecBuf and the
   // record layout).  xo[ks]: k/q row 16 ti + c (ti added as 4096 ti), key
   // channels 32 ks + 8 q4 .. +7.  mA: T/P rows 16 ti + c < 32, columns
@@ -744,10 +736,15 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
                 : f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (role == 2) {
-    // Load waves.  Chunk j+1 is written into the buffer of chunk j-1 after the
-    // first barrier of iteration j (the other waves are then done with that
-    // buffer) and is complete at the second.  Its global loads were issued
-    // during iteration j-1, so their latency is hidden.
+    // Load waves.  Chunk j+1 goes into the buffer of chunk j-1, in two parts:
+    //   after the first barrier of iteration j (the other waves are then done
+    //   with that buffer): its k, q and v, which the state waves read right
+    //   after the second barrier;
+    //   after the second barrier: its record and factors, first read after
+    //   the first barrier of iteration j+1 (T and factors, state waves) and
+    //   after its second (P, output waves).
+    // Each part's global loads for chunk j+2 are issued right after its put,
+    // so their latency is hidden behind a whole iteration.
     u32x4 stage[kLoadsPerWave];
     auto fetch = [&](int cc, int jc, int jj0, int jj1) {
       const int Lc = min(kC, eos - cc);
@@ -755,26 +752,40 @@ __global__ __launch_bounds__(kRecNT) void chunk_rec_kernel(ChunkArgs a, const un
       const unsigned char* nq = reinterpret_cast<const unsigned char*>(qg + (size_t)cc * kqts);
       const unsigned char* nv = reinterpret_cast<const unsigned char*>(vg + (size_t)cc * vts);
       const unsigned char* nr = recs + (size_t)jc * rstride;
-      if (Lc == kC) rec_fetch<true>(stage, nk, nq, nr, nv, ln, wave, lane, row_bytes, vrow_bytes, kC, jj0, jj1);
-      else rec_fetch<false>(stage, nk, nq, nr, nv, ln, wave, lane, row_bytes, vrow_bytes, Lc, jj0, jj1);
+      rec_fetch(stage, nk, nq, nr, nv, ln, wave, lane, row_bytes, vrow_bytes, Lc, jj0, jj1);
+      __builtin_amdgcn_sched_barrier(0);  // keep the groups in issue order
     };
+    // jj ranges: k, q [0, kKQV); record [kKQV, kVj); factors kVj - 1; v [kVj, end)
+    constexpr int kKQV = kBlkM / 2, kVj = kBlkV / 2;
+    // Every iteration issues the same loads in the same order -- v, k and q,
+    // then record and factors -- with chunks past the last one clamped to it
+    // (loaded, put into the dead buffer, never read).  With no branch around
+    // the loads the compiler counts the loads in flight exactly across
+    // iterations, so no put waits for a load issued after it (with branches,
+    // the put after the second barrier waited for the k, q and v loads
+    // issued just before that barrier).
+    const int last_c = bos + ((eos - bos - 1) / kC) * kC, last_j = jb + (eos - bos - 1) / kC;
     if (bos < eos) {
       fetch(bos, jb, 0, kLoadsPerWave);
       rec_put(bufs, stage, wave, lane);
-      if (bos + kC < eos) fetch(bos + kC, jb + 1, 0, kLoadsPerWave);
+      const int c1 = min(bos + kC, last_c), j1 = min(jb + 1, last_j);
+      fetch(c1, j1, kVj, kLoadsPerWave);
+      fetch(c1, j1, 0, kKQV);
+      fetch(c1, j1, kKQV, kVj);
     }
     lds_barrier();
     int it = 0;
     for (int c0 = bos, j = jb; c0 < eos; c0 += kC, ++j, ++it) {
       lds_barrier();
-      if (c0 + kC < eos) rec_put(bufs + ((it & 1) ^ 1), stage, wave, lane);
-      // the record, factor and v blocks (from HBM) right away, the k and q
-      // blocks (shared with neighbouring workgroups through L2) after the
-      // second barrier
-      constexpr int kKQ = kBlkM / 2;
-      if (c0 + 2 * kC < eos) fetch(c0 + 2 * kC, j + 2, kKQ, kLoadsPerWave);
+      RecBuf* nb = bufs + ((it & 1) ^ 1);
+      const int c2 = min(c0 + 2 * kC, last_c), j2 = min(j + 2, last_j);
+      rec_put(nb, stage, wave, lane, 0, kKQV);
+      rec_put(nb, stage, wave, lane, kVj, kLoadsPerWave);
+      fetch(c2, j2, kVj, kLoadsPerWave);
+      fetch(c2, j2, 0, kKQV);
       lds_barrier();
-      if (c0 + 2 * kC < eos) fetch(c0 + 2 * kC, j + 2, 0, kKQ);
+      rec_put(nb, stage, wave, lane, kKQV, kVj);
+      fetch(c2, j2, kKQV, kVj);
     }
     return;
   }
