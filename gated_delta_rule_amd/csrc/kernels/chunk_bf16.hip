@@ -233,8 +233,8 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
 }
 
 // ---------------------------------------------------------------------------
-// Chunk preparation: T = (I + A)^{-1}, P and token factors of one
-// (chunk, value head).
+// Chunk preparation: T = (I + A)^{-1}, P and token factors of every value
+// head of one (chunk, key head).
 
 // LDS of chunk_prep_kernel (36 KiB, so four workgroups share a compute
 // unit): k and q rows are dead once the Gram tiles are in registers, so A and
@@ -261,54 +261,37 @@ __global__ __launch_bounds__(kNT, 4) void chunk_prep_kernel(ChunkArgs a, unsigne
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int c = lane & 15, q4 = lane >> 4;
-  // Workgroup -> (chunk j, value head h), heads fastest and XCD-aware (see
-  // chunk_rec_kernel): the three value heads of a key head run side by side
-  // on one XCD, so two of them read the chunk's k and q from its L2.
+  // Workgroup -> (chunk j, key head kh), spread over the XCDs in contiguous
+  // runs.  The Gram tiles depend only on k and q, so they are formed once
+  // and serve the G = Hv / Hk value heads of the key head in turn.
   const int total = (int)gridDim.x;
   int lin = blockIdx.x;
   if (total % kXcds == 0) lin = (lin % kXcds) * (total / kXcds) + lin / kXcds;
-  const int j = lin / a.Hv, h = lin % a.Hv;
+  const int j = lin / a.Hk, kh = lin % a.Hk;
+  const int G = a.Hv / a.Hk;
   const int32_t* table = reinterpret_cast<const int32_t*>(ws);
   const ChunkPos pos = locate_chunk(a, table, j);
   if (!pos.valid) return;
   const int c0 = pos.c0, L = pos.L;
-  const int kh = h / (a.Hv / a.Hk);
-  unsigned char* rec = ws + kTableBytes(a.N) + ((size_t)j * a.Hv + h) * kRecBytes;
-  uint16_t* Thg = reinterpret_cast<uint16_t*>(rec);
-  uint16_t* Tlg = reinterpret_cast<uint16_t*>(rec + kMatBytes);
-  uint16_t* Phg = reinterpret_cast<uint16_t*>(rec + 2 * kMatBytes);
-  uint16_t* Plg = reinterpret_cast<uint16_t*>(rec + 3 * kMatBytes);
-  float* facg = reinterpret_cast<float*>(rec + kFacOff);
+  // g (wave 0) or beta (wave 1) of token `lane` of value head kh*G + hh
+  auto load_gb = [&](int hh) {
+    return (wave < 2 && lane < L) ? (wave == 0 ? a.g : a.beta)[(size_t)(c0 + lane) * a.Hv + kh * G + hh] : 0.f;
+  };
+  float gnext = load_gb(0);
 
-  // ---- k, q rows to LDS with permuted columns; g, beta
+  // ---- k, q rows to LDS with permuted columns
   {
     const uint16_t* src = static_cast<const uint16_t*>(tid < 128 ? a.k : a.q);
     uint16_t(*X)[kD + 8] = tid < 128 ? sm.Kr : sm.Qr;
     const int b = tid & 127, rb = b >> 4, cb = b & 15;
     const int pc = perm8(cb);
-    // g (wave 0) or beta (wave 1) of token `lane` first, then all eight k/q
-    // loads in flight before the LDS stores; rows past L read row L-1 (in
-    // bounds) and are zeroed
-    float gv = 0.f;
-    if (wave < 2 && lane < L) gv = (wave == 0 ? a.g : a.beta)[(size_t)(c0 + lane) * a.Hv + h];
+    // all eight k/q loads in flight before the LDS stores; rows past L read
+    // row L-1 (in bounds) and are zeroed
     u32x4 w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = min(8 * rb + i, L - 1);
       w[i] = *reinterpret_cast<const u32x4*>(src + ((size_t)(c0 + row) * a.Hk + kh) * kD + 8 * cb);
-    }
-    if (wave == 1) sm.bin[lane] = gv;
-    if (wave == 0) {
-      gv = gv < kMinLogDecay ? kMinLogDecay : gv;  // (a NaN stays NaN)
-      // chunk-local cumulative log-decay, summed in fp64 while the k/q loads
-      // are in flight; kept as log2 (G * log2 e)
-      double G = (double)gv;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const double o = __shfl_up(G, off, 64);
-        if (lane >= off) G += o;
-      }
-      sm.G2[lane] = (float)(G * 1.4426950408889634);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -355,142 +338,169 @@ __global__ __launch_bounds__(kNT, 4) void chunk_prep_kernel(ChunkArgs a, unsigne
   }
   lds_barrier();
 
-  // ---- per-token factors (wave 0): norms and scales
-  if (wave == 0) {
-    const float rkv = a.use_l2 ? 1.f / sqrtf(sm.ssk[lane] + a.eps) : 1.f;
-    const float rqv = a.use_l2 ? 1.f / sqrtf(sm.ssq[lane] + a.eps) : 1.f;
-    const float g2 = sm.G2[lane];
-    const float g2L = sm.G2[63];
-    const float eG = exp2f(g2);
-    const float bv = sm.bin[lane];
-    sm.rk[lane] = rkv;
-    sm.ar[lane] = bv * rkv;
-    sm.pr[lane] = a.scale * rqv;
-    facg[lane] = bv;                         // bt
-    facg[64 + lane] = bv * eG * rkv;         // xr
-    facg[128 + lane] = a.scale * rqv * eG;   // yq
-    facg[192 + lane] = rkv * exp2f(g2L - g2);  // cL
-    if (lane == 0) facg[256] = exp2f(g2L);   // e^{G_L}
-  }
-  lds_barrier();
-
-  // ---- scale Gram tiles into A (fp32, LDS) and P (hi/lo bf16, workspace)
+  for (int hh = 0; hh < G; ++hh) {
+    const int h = kh * G + hh;
+    unsigned char* rec = ws + kTableBytes(a.N) + ((size_t)j * a.Hv + h) * kRecBytes;
+    uint16_t* Thg = reinterpret_cast<uint16_t*>(rec);
+    uint16_t* Tlg = reinterpret_cast<uint16_t*>(rec + kMatBytes);
+    uint16_t* Phg = reinterpret_cast<uint16_t*>(rec + 2 * kMatBytes);
+    uint16_t* Plg = reinterpret_cast<uint16_t*>(rec + 3 * kMatBytes);
+    float* facg = reinterpret_cast<float*>(rec + kFacOff);
+    {
+      float gv = gnext;
+      if (hh + 1 < G) gnext = load_gb(hh + 1);  // the next head's, a whole head ahead
+      if (wave == 1) sm.bin[lane] = gv;
+      if (wave == 0) {
+        gv = gv < kMinLogDecay ? kMinLogDecay : gv;  // (a NaN stays NaN)
+        // chunk-local cumulative log-decay, summed in fp64; kept as log2 (G * log2 e)
+        double Gs = (double)gv;
 #pragma unroll
-  for (int u = 0; u < 5; ++u) {
-    const int job = wave + 4 * u;
-    if (job >= 20) break;
-    const int ti = gti[u], tj = gtj[u];
-    const int i = 16 * ti + c, j0 = 16 * tj + 4 * q4;
-    const float g2i = sm.G2[i];
-    const f32x4 g2j = *reinterpret_cast<const f32x4*>(&sm.G2[j0]);
-    const f32x4 rkj = *reinterpret_cast<const f32x4*>(&sm.rk[j0]);
-    const float rowf = job < 10 ? sm.ar[i] : sm.pr[i];
-    f32x4 val;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int jj = j0 + e;
-      const bool keep = job < 10 ? (jj < i) : (jj <= i);
-      // exponent <= 0 where kept; the hardware exp2 may flush results below
-      // 2^-126 to zero, far under the precision these entries carry
-      const float x = rowf * rkj[e] * __builtin_amdgcn_exp2f(g2i - g2j[e]) * gacc[u][e];
-      val[e] = keep ? x : 0.f;
-    }
-    if (job < 10) {
-      *reinterpret_cast<f32x4*>(&sm.A[i][j0]) = val;
-    } else {
-      u32x2 hi, lo;
-      split4(val, hi, lo);
-      const int off = compact_idx(i, perm32(j0));
-      *reinterpret_cast<u32x2*>(Phg + off) = hi;
-      *reinterpret_cast<u32x2*>(Plg + off) = lo;
-    }
-  }
-  // zero the above-diagonal tiles (0,1) and (2,3) that 32-wide steps read
-  if (wave < 2) {
-    const int i = 32 * wave + c;
-    const int off = compact_idx(i, perm32(32 * wave + 16 + 4 * q4));
-    *reinterpret_cast<u32x2*>(Phg + off) = u32x2{0u, 0u};
-    *reinterpret_cast<u32x2*>(Plg + off) = u32x2{0u, 0u};
-    *reinterpret_cast<f32x4*>(&sm.Tf[i][32 * wave + 16 + 4 * q4]) = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  lds_barrier();
-
-  // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution
-  // (wave w inverts block w; lane c < 16 computes column c)
-  if (lane < 16) {
-    const int b = wave;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-#pragma unroll
-    for (int r = 1; r < 16; ++r) {
-      const float* arow = &sm.A[16 * b + r][16 * b];
-      float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-      for (int m4 = 0; m4 < r; m4 += 4) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(arow + m4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (m4 + e < r) {
-            if (e & 1) s1 += av[e] * x[m4 + e];
-            else s0 += av[e] * x[m4 + e];
-          }
+        for (int off = 1; off < 64; off <<= 1) {
+          const double o = __shfl_up(Gs, off, 64);
+          if (lane >= off) Gs += o;
+        }
+        sm.G2[lane] = (float)(Gs * 1.4426950408889634);
       }
-      x[r] = (r > c) ? -(s0 + s1) : x[r];
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sm.Tf[16 * b + r][16 * b + c] = x[r];
-  }
-  lds_barrier();
-  // level 1: T_{p+1,p} = -T_{p+1,p+1} (A_{p+1,p} T_{p,p}), p = 0, 32 (waves 0, 1)
-  if (wave < 2) {
-    const int p = 32 * wave;
-    const f32x4 y = tile_mm_f32<16>(&sm.A[p + 16][p], kC + 4, &sm.Tf[p][p], kC + 4, c, q4);
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) sm.A[16 * wave + 4 * q4 + i4][32 + c] = y[i4];
-  }
-  lds_barrier();
-  if (wave < 2) {
-    const int p = 32 * wave;
-    const f32x4 t = tile_mm_f32<16>(&sm.Tf[p + 16][p + 16], kC + 4, &sm.A[16 * wave][32], kC + 4, c, q4);
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) sm.Tf[p + 16 + 4 * q4 + i4][p + c] = -t[i4];
-  }
-  lds_barrier();
-  // level 2: T_{2:4,0:2} = -T_{2:4,2:4} (A_{2:4,0:2} T_{0:2,0:2}), one 16x16 tile per wave
-  {
-    const int yi = wave >> 1, yj = wave & 1;
-    const f32x4 y = tile_mm_f32<32>(&sm.A[32 + 16 * yi][0], kC + 4, &sm.Tf[0][16 * yj], kC + 4, c, q4);
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) sm.A[16 * yi + 4 * q4 + i4][32 + 16 * yj + c] = y[i4];
-  }
-  lds_barrier();
-  {
-    const int xi = wave >> 1, xj = wave & 1;
-    const f32x4 t = tile_mm_f32<32>(&sm.Tf[32 + 16 * xi][32], kC + 4, &sm.A[0][32 + 16 * xj], kC + 4, c, q4);
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) sm.Tf[32 + 16 * xi + 4 * q4 + i4][16 * xj + c] = -t[i4];
-  }
-  lds_barrier();
-  // T to hi/lo bf16 over the lower 32x32-block triangle (the upper parts of
-  // the diagonal blocks are zero and are read by 32-wide steps)
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const int gidx = tid + kNT * k;  // 768 groups of 4: rows 0..31 x 8, rows 32..63 x 16
-    int i, j0;
-    if (gidx < 256) {
-      i = gidx >> 3;
-      j0 = 4 * (gidx & 7);
-    } else {
-      i = 32 + ((gidx - 256) >> 4);
-      j0 = 4 * ((gidx - 256) & 15);
+    lds_barrier();
+
+    // ---- per-token factors (wave 0): norms and scales
+    if (wave == 0) {
+      const float rkv = a.use_l2 ? 1.f / sqrtf(sm.ssk[lane] + a.eps) : 1.f;
+      const float rqv = a.use_l2 ? 1.f / sqrtf(sm.ssq[lane] + a.eps) : 1.f;
+      const float g2 = sm.G2[lane];
+      const float g2L = sm.G2[63];
+      const float eG = exp2f(g2);
+      const float bv = sm.bin[lane];
+      sm.rk[lane] = rkv;
+      sm.ar[lane] = bv * rkv;
+      sm.pr[lane] = a.scale * rqv;
+      facg[lane] = bv;                         // bt
+      facg[64 + lane] = bv * eG * rkv;         // xr
+      facg[128 + lane] = a.scale * rqv * eG;   // yq
+      facg[192 + lane] = rkv * exp2f(g2L - g2);  // cL
+      if (lane == 0) facg[256] = exp2f(g2L);   // e^{G_L}
     }
-    u32x2 hi, lo;
-    split4(*reinterpret_cast<const f32x4*>(&sm.Tf[i][j0]), hi, lo);
-    const int off = compact_idx(i, perm32(j0));
-    *reinterpret_cast<u32x2*>(Thg + off) = hi;
-    *reinterpret_cast<u32x2*>(Tlg + off) = lo;
-  }
+    lds_barrier();
+
+    // ---- scale Gram tiles into A (fp32, LDS) and P (hi/lo bf16, workspace)
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+      const int job = wave + 4 * u;
+      if (job >= 20) break;
+      const int ti = gti[u], tj = gtj[u];
+      const int i = 16 * ti + c, j0 = 16 * tj + 4 * q4;
+      const float g2i = sm.G2[i];
+      const f32x4 g2j = *reinterpret_cast<const f32x4*>(&sm.G2[j0]);
+      const f32x4 rkj = *reinterpret_cast<const f32x4*>(&sm.rk[j0]);
+      const float rowf = job < 10 ? sm.ar[i] : sm.pr[i];
+      f32x4 val;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int jj = j0 + e;
+        const bool keep = job < 10 ? (jj < i) : (jj <= i);
+        // exponent <= 0 where kept; the hardware exp2 may flush results below
+        // 2^-126 to zero, far under the precision these entries carry
+        const float x = rowf * rkj[e] * __builtin_amdgcn_exp2f(g2i - g2j[e]) * gacc[u][e];
+        val[e] = keep ? x : 0.f;
+      }
+      if (job < 10) {
+        *reinterpret_cast<f32x4*>(&sm.A[i][j0]) = val;
+      } else {
+        u32x2 hi, lo;
+        split4(val, hi, lo);
+        const int off = compact_idx(i, perm32(j0));
+        *reinterpret_cast<u32x2*>(Phg + off) = hi;
+        *reinterpret_cast<u32x2*>(Plg + off) = lo;
+      }
+    }
+    // zero the above-diagonal tiles (0,1) and (2,3) that 32-wide steps read
+    if (wave < 2) {
+      const int i = 32 * wave + c;
+      const int off = compact_idx(i, perm32(32 * wave + 16 + 4 * q4));
+      *reinterpret_cast<u32x2*>(Phg + off) = u32x2{0u, 0u};
+      *reinterpret_cast<u32x2*>(Plg + off) = u32x2{0u, 0u};
+      *reinterpret_cast<f32x4*>(&sm.Tf[i][32 * wave + 16 + 4 * q4]) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    lds_barrier();
+
+    // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution
+    // (wave w inverts block w; lane c < 16 computes column c)
+    if (lane < 16) {
+      const int b = wave;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+#pragma unroll
+      for (int r = 1; r < 16; ++r) {
+        const float* arow = &sm.A[16 * b + r][16 * b];
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int m4 = 0; m4 < r; m4 += 4) {
+          const f32x4 av = *reinterpret_cast<const f32x4*>(arow + m4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (m4 + e < r) {
+              if (e & 1) s1 += av[e] * x[m4 + e];
+              else s0 += av[e] * x[m4 + e];
+            }
+        }
+        x[r] = (r > c) ? -(s0 + s1) : x[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.Tf[16 * b + r][16 * b + c] = x[r];
+    }
+    lds_barrier();
+    // level 1: T_{p+1,p} = -T_{p+1,p+1} (A_{p+1,p} T_{p,p}), p = 0, 32 (waves 0, 1)
+    if (wave < 2) {
+      const int p = 32 * wave;
+      const f32x4 y = tile_mm_f32<16>(&sm.A[p + 16][p], kC + 4, &sm.Tf[p][p], kC + 4, c, q4);
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) sm.A[16 * wave + 4 * q4 + i4][32 + c] = y[i4];
+    }
+    lds_barrier();
+    if (wave < 2) {
+      const int p = 32 * wave;
+      const f32x4 t = tile_mm_f32<16>(&sm.Tf[p + 16][p + 16], kC + 4, &sm.A[16 * wave][32], kC + 4, c, q4);
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) sm.Tf[p + 16 + 4 * q4 + i4][p + c] = -t[i4];
+    }
+    lds_barrier();
+    // level 2: T_{2:4,0:2} = -T_{2:4,2:4} (A_{2:4,0:2} T_{0:2,0:2}), one 16x16 tile per wave
+    {
+      const int yi = wave >> 1, yj = wave & 1;
+      const f32x4 y = tile_mm_f32<32>(&sm.A[32 + 16 * yi][0], kC + 4, &sm.Tf[0][16 * yj], kC + 4, c, q4);
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) sm.A[16 * yi + 4 * q4 + i4][32 + 16 * yj + c] = y[i4];
+    }
+    lds_barrier();
+    {
+      const int xi = wave >> 1, xj = wave & 1;
+      const f32x4 t = tile_mm_f32<32>(&sm.Tf[32 + 16 * xi][32], kC + 4, &sm.A[0][32 + 16 * xj], kC + 4, c, q4);
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) sm.Tf[32 + 16 * xi + 4 * q4 + i4][16 * xj + c] = -t[i4];
+    }
+    lds_barrier();
+    // T to hi/lo bf16 over the lower 32x32-block triangle (the upper parts of
+    // the diagonal blocks are zero and are read by 32-wide steps)
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int gidx = tid + kNT * k;  // 768 groups of 4: rows 0..31 x 8, rows 32..63 x 16
+      int i, j0;
+      if (gidx < 256) {
+        i = gidx >> 3;
+        j0 = 4 * (gidx & 7);
+      } else {
+        i = 32 + ((gidx - 256) >> 4);
+        j0 = 4 * ((gidx - 256) & 15);
+      }
+      u32x2 hi, lo;
+      split4(*reinterpret_cast<const f32x4*>(&sm.Tf[i][j0]), hi, lo);
+      const int off = compact_idx(i, perm32(j0));
+      *reinterpret_cast<u32x2*>(Thg + off) = hi;
+      *reinterpret_cast<u32x2*>(Tlg + off) = lo;
+    }
+  }  // value heads
 }
 
 // ---------------------------------------------------------------------------
@@ -1034,7 +1044,7 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, void* workspace, hipStream_t st
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_prep_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)(nch * a.Hv)), dim3(kNT), smem, st, a, ws);
+    hipLaunchKernelGGL(chunk_prep_kernel, dim3((unsigned)(nch * a.Hk)), dim3(kNT), smem, st, a, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
