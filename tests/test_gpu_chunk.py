@@ -67,6 +67,20 @@ def test_varlen_packed_with_empty_and_short_sequences():
     _check(x, cu=cu, s0=s0)
 
 
+@pytest.mark.parametrize("hk,hv", [(4, 4), (2, 8), (3, 24)])
+def test_head_ratios_varlen(hk, hv):
+    """Value heads per key head G = 1, 4 and 8: the prepare kernel forms each
+    (chunk, key head)'s Gram tiles once and serves its G value heads in turn,
+    and the recurrence groups a key head's workgroups on one XCD.  Ragged
+    packed lengths with an initial state, against the oracle."""
+    lens = [1, 200, 64, 65, 0, 131]
+    cu = synth.cu_seqlens_of(lens)
+    x = synth.gdr_inputs(40 + hv, B=1, T=int(cu[-1]), hk=hk, hv=hv, d=128, dtype="bf16")
+    s0 = (0.05 * np.random.default_rng(41 + hv).standard_normal((len(lens), hv, 128, 128))).astype(np.float32)
+    say(f"chunk varlen {lens} heads {hk}/{hv}")
+    _check(x, cu=cu, s0=s0)
+
+
 def test_varlen_packed_equals_separate_bit_exact():
     import torch
     lens = [70, 1, 129, 64]
