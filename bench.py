@@ -486,7 +486,7 @@ def bench_attention(reps: int = 3, dec_steps: int = 20):
 
     N, L = 64, 32768
     kc = torch.randn((N, L, Hk, Da), device=dev, generator=gen).to(torch.bfloat16)
-    vc = torch.randn((N, Hk, Da, L), device=dev, generator=gen).to(torch.bfloat16)
+    vc = torch.randn((N, Hk, L // 32, Da, 32), device=dev, generator=gen).to(torch.bfloat16)
     lens = torch.randint(32000, L - dec_steps, (N,), device=dev, generator=gen, dtype=torch.int32)
     qd, kd, vd, gd = rnd(N, Hq, Da), rnd(N, Hk, Da), rnd(N, Hk, Da), rnd(N, Hq, Da)
     od = torch.empty_like(qd)

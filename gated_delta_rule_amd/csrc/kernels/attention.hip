@@ -112,11 +112,20 @@ struct PrepArgs {
   uint16_t* q_rot;               // [rows, Hq, D]
   uint16_t* k_pad;               // prefill: [64 * chunks, Hk, D] or NULL
   uint16_t* k_rot;               // [rows, Hk, D] or NULL (the rotated k, unpadded)
-  uint16_t *k_cache, *v_cache;   // [N, cache_len, Hk, D] or NULL
+  uint16_t *k_cache, *v_cache;   // [N, cache_len, Hk, D] and the blocked layout below, or NULL
   int rows, N, Hq, Hk, cache_len;
   float eps;
   double base;
 };
+
+// Decode V cache [N, Hk, cache_len / 32, 256, 32]: key 32 b + k of dim d
+// sits in block b, row d, at position vc_pos(k), so that the 8 keys one lane
+// of the decode's value product needs -- {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3}
+// for lane group g -- are one 16-byte read, and a 16-row read is 1 KiB.
+__host__ __device__ constexpr int vc_pos(int k) { return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3); }
+__device__ __forceinline__ size_t vc_index(int n, int h, int Hk, int cache_len, int d, int key) {
+  return ((((size_t)n * Hk + h) * (cache_len / 32) + (key >> 5)) * kAD + d) * 32 + vc_pos(key & 31);
+}
 
 __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
   __shared__ float s_cos[kRot / 2], s_sin[kRot / 2];
@@ -185,11 +194,11 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
         const size_t c = ((size_t)n * a.cache_len + pos) * a.Hk + h;
         *reinterpret_cast<u32x2*>(a.k_cache + c * kAD + 4 * lane) = out;
         if (!a.cu) {
-          // decode: the token's v into the transposed cache, one key column
+          // decode: the token's v into the blocked cache, one key column
           const u16x4 vv = *reinterpret_cast<const u16x4*>(a.v + ((size_t)t * a.Hk + h) * kAD + 4 * lane);
-          uint16_t* vc = a.v_cache + (((size_t)n * a.Hk + h) * kAD + 4 * lane) * a.cache_len + pos;
+          uint16_t* vc = a.v_cache + vc_index(n, h, a.Hk, a.cache_len, 4 * lane, pos);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vc[(size_t)e * a.cache_len] = vv[e];
+          for (int e = 0; e < 4; ++e) vc[32 * e] = vv[e];
         }
       }
     }
@@ -238,20 +247,23 @@ __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* v, const i
     *reinterpret_cast<u16x8*>(dst) = pk;
   }
   if (v_cache) {
-    // [N, Hk, D, cache_len]: this chunk's keys k0 .. k0+63 of row d, natural
-    // order, only positions inside the sequence and the cache
-    uint16_t* vc = v_cache + (((size_t)n * Hk + h) * kAD + d) * cache_len;
+    // the blocked decode cache: this chunk's keys k0 .. k0+63 of row d (two
+    // 32-key blocks), only positions inside the sequence and the cache
     const int kend = min(L, cache_len) - k0;
     if (kend >= kKB) {
 #pragma unroll
-      for (int s = 0; s < kKB; s += 8) {
-        u16x8 pk;
+      for (int b = 0; b < 2; ++b) {
+        uint16_t* vc = v_cache + vc_index(n, h, Hk, cache_len, d, k0 + 32 * b);  // position 0 of the block
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pk[e] = tile[s + e][d];
-        *reinterpret_cast<u16x8*>(vc + k0 + s) = pk;
+        for (int g = 0; g < 4; ++g) {
+          u16x8 pk;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk[e] = tile[32 * b + 4 * g + (e & 3) + 16 * (e >> 2)][d];
+          *reinterpret_cast<u16x8*>(vc + 8 * g) = pk;
+        }
       }
     } else {
-      for (int s = 0; s < kend; ++s) vc[k0 + s] = tile[s][d];
+      for (int s = 0; s < kend; ++s) v_cache[vc_index(n, h, Hk, cache_len, d, k0 + s)] = tile[s][d];
     }
   }
 }
@@ -480,7 +492,6 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
 // their uses).  The split's running maximum, sum and unnormalised output go
 // to a workspace; attn_combine_kernel merges the splits and applies the gate.
 typedef float f32x4v __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
 // Keys per split: 256 .. 2048 (a multiple of 64), chosen on the host so that
 // a step has about 8192 waves.
@@ -532,7 +543,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecArgs a) {
   for (int i = 0; i < 16; ++i) o[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lsum = 0.f;
   const uint16_t* kbase = a.k_cache + ((size_t)n * a.cache_len * a.Hk + kvh) * kAD + 8 * grp;
-  const uint16_t* vbase = a.v_cache + ((size_t)n * a.Hk + kvh) * kAD * a.cache_len + 4 * grp;
+  const uint16_t* vbase = a.v_cache + ((size_t)n * a.Hk + kvh) * kAD * a.cache_len + 8 * grp;
   const int kend = min(kb + a.split_keys, len);
   for (int k0 = kb; k0 < kend; k0 += 32) {
     bf16x8 kf[16];
@@ -550,14 +561,12 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[8 * t + ks], qf[ks], s[t], 0, 0, 0);
     }
-    // V^T fragments: dim row 16 dt + col, keys 4 grp .. +3 and 16 + 4 grp .. +3
-    u32x2v vf[16][2];
+    // V^T fragments: dim row 16 dt + col, keys 4 grp .. +3 and 16 + 4 grp .. +3,
+    // one 16-byte read from the blocked cache (16 rows: 1 KiB contiguous)
+    u32x4 vf[16];
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
-      const uint16_t* vrow = vbase + (size_t)(16 * dt + col) * a.cache_len + k0;
-      vf[dt][0] = *reinterpret_cast<const u32x2v*>(vrow);
-      vf[dt][1] = *reinterpret_cast<const u32x2v*>(vrow + 16);
-    }
+    for (int dt = 0; dt < 16; ++dt)
+      vf[dt] = *reinterpret_cast<const u32x4*>(vbase + ((size_t)(k0 >> 5) * kAD + 16 * dt + col) * 32);
     __builtin_amdgcn_sched_barrier(0);
     float bmax = -INFINITY;
 #pragma unroll
@@ -593,7 +602,7 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecArgs a) {
     const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
-      const bf16x8 af = __builtin_bit_cast(bf16x8, u32x4{vf[dt][0][0], vf[dt][0][1], vf[dt][1][0], vf[dt][1][1]});
+      const bf16x8 af = __builtin_bit_cast(bf16x8, vf[dt]);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, o[dt], 0, 0, 0);
     }
   }

@@ -441,8 +441,9 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.
 
     q, gate: [T, Hq, 256] bf16; k, v: [T, Hk, 256] bf16; norm weights [256]
     fp32; cu_seqlens int32 [N+1]; optional k_cache [N, L, Hk, 256] and
-    v_cache [N, Hk, 256, L] bf16 (L a multiple of 64) receive the rotated keys
-    and the values.  Returns out [T, Hq, 256] bf16.
+    v_cache [N, Hk, L / 32, 256, 32] bf16 (L a multiple of 64; the blocked
+    layout include/gdr.h defines) receive the rotated keys and the values.
+    Returns out [T, Hq, 256] bf16.
     """
     dev = q.device
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate")):
@@ -460,8 +461,8 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.
         _need(k_cache, "k_cache", (torch.bfloat16,), dev)
         _need(v_cache, "v_cache", (torch.bfloat16,), dev)
         cache_len = k_cache.shape[1]
-        if k_cache.shape != (N, cache_len, Hk, D) or v_cache.shape != (N, Hk, D, cache_len):
-            raise ValueError(f"caches must be [N, L, {Hk}, {D}] and [N, {Hk}, {D}, L]")
+        if k_cache.shape != (N, cache_len, Hk, D) or v_cache.shape != (N, Hk, cache_len // 32, D, 32):
+            raise ValueError(f"caches must be [N, L, {Hk}, {D}] and [N, {Hk}, L / 32, {D}, 32]")
     d = attn_desc(T, N, Hq, Hk, D, cache_len, eps, rope_base)
     if workspace is None:
         nb = ctypes.c_size_t(0)
@@ -503,7 +504,7 @@ def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.T
     """One decode token per sequence (gdr_attn_decode).
 
     q, gate: [N, Hq, 256]; k, v: [N, Hk, 256] bf16; k_cache [N, L, Hk, 256],
-    v_cache [N, Hk, 256, L] bf16 updated in place at cache_lens[n];
+    v_cache [N, Hk, L / 32, 256, 32] bf16 updated in place at cache_lens[n];
     cache_lens int32 [N] (not advanced).  Returns out [N, Hq, 256] bf16.
     """
     dev = q.device
@@ -516,7 +517,8 @@ def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gate: torch.T
     Hk = k.shape[1]
     L = k_cache.shape[1]
     if k.shape != (N, Hk, D) or v.shape != (N, Hk, D) or gate.shape != (N, Hq, D) \
-            or k_cache.shape != (N, L, Hk, D) or v_cache.shape != (N, Hk, D, L) or cache_lens.shape != (N,):
+            or k_cache.shape != (N, L, Hk, D) or v_cache.shape != (N, Hk, L // 32, D, 32) \
+            or cache_lens.shape != (N,):
         raise ValueError("shape mismatch in attention decode inputs")
     d = attn_desc(N, N, Hq, Hk, D, L, eps, rope_base)
     if workspace is None:

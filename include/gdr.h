@@ -432,11 +432,16 @@ gdr_status gdr_attn_prefill_workspace_size(const gdr_attn_desc* d, size_t* bytes
  *   cu_seqlens   [N+1] int32 device array (positions restart at 0 in each sequence)
  *   out          [T, Hq, 256] bf16
  *   k_cache      [N, cache_len, Hk, 256] bf16 and
- *   v_cache      [N, Hk, 256, cache_len] bf16 (keys contiguous), or both NULL:
- *                when given, position p of sequence n receives its token p's
- *                k' and v, for every p < cache_len (ready for gdr_attn_decode);
+ *   v_cache      [N, Hk, cache_len / 32, 256, 32] bf16, or both NULL: when
+ *                given, position p of sequence n receives its token p's k'
+ *                and v, for every p < cache_len (ready for gdr_attn_decode);
  *                other positions are not written.  cache_len must be a
  *                multiple of 64.
+ *                v_cache is blocked by 32 positions: position 32 b + i of
+ *                dim d is element [n][h][b][d][8 ((i mod 16) / 4) +
+ *                4 (i / 16) + i mod 4], the order in which the decode's value
+ *                product takes the keys, so it reads each block as one
+ *                contiguous 16 KiB run.
  *   workspace    >= gdr_attn_prefill_workspace_size bytes, 256-byte aligned
  * Errors: INVALID_ARG for NULL required pointers, misalignment (16 bytes),
  * a short workspace, one cache pointer without the other, cache_len not a
@@ -452,17 +457,19 @@ gdr_status gdr_attn_decode_workspace_size(const gdr_attn_desc* d, size_t* bytes)
 /*
  * One decode token per sequence (d->num_tokens = d->num_seqs = N):
  *   q, gate      [N, Hq, 256] bf16;  k, v [N, Hk, 256] bf16 (the new token)
- *   k_cache      [N, cache_len, Hk, 256] bf16, v_cache [N, Hk, 256, cache_len]
- *                bf16 (the layout gdr_attn_prefill fills), updated IN PLACE:
- *                the token's k' and v are written at position cache_lens[n]
+ *   k_cache      [N, cache_len, Hk, 256] bf16, v_cache [N, Hk, cache_len / 32,
+ *                256, 32] bf16 (the layouts gdr_attn_prefill fills), updated IN
+ *                PLACE: the token's k' and v are written at position
+ *                cache_lens[n]
  *   cache_lens   [N] int32 device array: tokens already cached; the token sits
  *                at that position and attends to positions 0 .. cache_lens[n].
  *                Must be < cache_len (trusted).  Not modified: the caller
  *                advances it.
  *   out          [N, Hq, 256] bf16
  *   workspace    >= gdr_attn_decode_workspace_size bytes, 256-byte aligned
- * The keys are split into pieces of 256 positions, each attended on its own
- * and merged (exactly the softmax over all of them, up to rounding).
+ * The keys are split into pieces of 256 to 2048 positions (chosen from N, Hk
+ * and cache_len), each attended on its own and merged: exactly the softmax
+ * over all of them, up to rounding.
  * Errors: as gdr_attn_prefill; INVALID_ARG also for cache_len <= 0.
  */
 gdr_status gdr_attn_decode(const gdr_attn_desc* d, const void* q, const void* k, const void* v, const void* gate,

@@ -65,3 +65,32 @@ def bits_equal(a, b) -> bool:
         return False
     iv = {torch.float32: torch.int32, torch.bfloat16: torch.int16}[a.dtype]
     return bool(torch.equal(a.view(iv), b.view(iv)))
+
+
+# The decode V cache is blocked by 32 positions (include/gdr.h): position
+# 32 b + i of dim d sits at [n][h][b][d][VC_POS[i]]; VC_KEY is the inverse.
+VC_POS = [8 * ((i % 16) // 4) + 4 * (i // 16) + i % 4 for i in range(32)]
+VC_KEY = [VC_POS.index(p) for p in range(32)]
+
+
+def _tp(x, dims):
+    return x.permute(*dims) if hasattr(x, "permute") else np.transpose(x, dims)
+
+
+def _contig(x):
+    return x.contiguous() if hasattr(x, "contiguous") else np.ascontiguousarray(x)
+
+
+def v_cache_blocked(vnat):
+    """Natural values [N, L, Hk, D] -> the decode V cache [N, Hk, L / 32, D, 32]
+    (numpy or torch)."""
+    N, L, Hk, D = vnat.shape
+    x = vnat.reshape(N, L // 32, 32, Hk, D)[:, :, VC_KEY]  # [N, b, position, Hk, D]
+    return _contig(_tp(x, (0, 3, 1, 4, 2)))
+
+
+def v_cache_natural(vb):
+    """The decode V cache [N, Hk, L / 32, D, 32] -> natural values [N, L, Hk, D]."""
+    N, Hk, B, D, _ = vb.shape
+    x = _tp(vb, (0, 2, 4, 1, 3))[:, :, VC_POS]  # [N, b, key, Hk, D]
+    return _contig(x.reshape(N, B * 32, Hk, D))

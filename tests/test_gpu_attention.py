@@ -18,7 +18,7 @@ import pytest
 
 from gated_delta_rule_amd import synth
 from oracle import attention as aref
-from helpers import bf16_ulp, bits_equal, gpu, say, to_dev, to_host
+from helpers import bf16_ulp, bits_equal, gpu, say, to_dev, to_host, v_cache_blocked, v_cache_natural
 
 pytestmark = pytest.mark.gpu
 
@@ -74,17 +74,18 @@ def test_prefill_against_oracle(lengths, hq, hk):
     q, k, v, g, qw, kw, cu = _dev(x, dev)
     L = (L + 63) // 64 * 64
     kc = torch.zeros((N, L, hk, 256), device=dev, dtype=torch.bfloat16)
-    vc = torch.zeros((N, hk, 256, L), device=dev, dtype=torch.bfloat16)
+    vc = torch.zeros((N, hk, L // 32, 256, 32), device=dev, dtype=torch.bfloat16)
     out = gdr.attn_prefill(q, k, v, g, qw, kw, cu, k_cache=kc, v_cache=vc)
     qo, ko = gdr.attn_qk_norm_rope(q, k, qw, kw, cu)
     torch.cuda.synchronize()
     r = aref.core_prefill(to_host(qo), to_host(ko), x.v, x.gate, x.cu_seqlens)
     _check_out(to_host(out), r["out"], r["mass"])
+    vn = v_cache_natural(vc)
     for n in range(N):
         a, b = x.cu_seqlens[n], x.cu_seqlens[n + 1]
         assert bits_equal(kc[n, :b - a], ko[a:b])
-        assert bits_equal(vc[n, :, :, :b - a], v[a:b].permute(1, 2, 0).contiguous())
-        assert not torch.any(kc[n, b - a:].float() != 0) and not torch.any(vc[n, :, :, b - a:].float() != 0)
+        assert bits_equal(vn[n, :b - a], v[a:b])
+        assert not torch.any(kc[n, b - a:].float() != 0) and not torch.any(vn[n, b - a:].float() != 0)
 
 
 def test_prefill_full_size_sampled():
@@ -151,24 +152,24 @@ def test_decode_against_oracle(lens, L, hq, hk):
     x = synth.attn_inputs(46, lengths=(1,) * N, hq=hq, hk=hk)
     rng = synth.rng(47)
     kc0 = synth.round_bf16(rng.standard_normal((N, L, hk, 256)))
-    vc0 = synth.round_bf16(rng.standard_normal((N, hk, 256, L)))
+    vc0 = synth.round_bf16(rng.standard_normal((N, L, hk, 256)))  # natural order
     say(f"attention decode lens {lens} L={L} Hq={hq} Hk={hk}")
     q, k, v, g, qw, kw, _ = _dev(x, dev)
-    kc, vc = to_dev(kc0, "bf16", dev), to_dev(vc0, "bf16", dev)
+    kc, vc = to_dev(kc0, "bf16", dev), to_dev(v_cache_blocked(vc0), "bf16", dev)
     cl = torch.tensor(lens, device=dev, dtype=torch.int32)
     out = gdr.attn_decode(q, k, v, g, qw, kw, kc, vc, cl)
     torch.cuda.synchronize()
-    kch, vch = to_host(kc), to_host(vc)
+    kch, vch = to_host(kc), v_cache_natural(to_host(vc))
     qrot = np.zeros((N, hq, 256))
     for n, p in enumerate(lens):
         qg, kg = _gpu_qrot_at(q[n], k[n], qw, kw, p, dev)
         qrot[n] = to_host(qg)
         assert bits_equal(kc[n, p], kg)
-        assert np.array_equal(vch[n, :, :, p], to_host(v[n]))
+        assert np.array_equal(vch[n, p], to_host(v[n]))
         keep = np.ones(L, bool)
         keep[p] = False
-        assert np.array_equal(kch[n, keep], kc0[n, keep]) and np.array_equal(vch[n][..., keep], vc0[n][..., keep])
-    r = aref.core_decode(qrot, x.gate, kch, vch.transpose(0, 3, 1, 2), np.asarray(lens) + 1)
+        assert np.array_equal(kch[n, keep], kc0[n, keep]) and np.array_equal(vch[n, keep], vc0[n, keep])
+    r = aref.core_decode(qrot, x.gate, kch, vch, np.asarray(lens) + 1)
     _check_out(to_host(out), r["out"], r["mass"])
 
 
@@ -183,7 +184,7 @@ def test_decode_continues_prefill():
     q, k, v, g, qw, kw, _ = _dev(x, dev)
     say("attention prefill 700 then decode 2")
     kc = torch.zeros((1, L, 4, 256), device=dev, dtype=torch.bfloat16)
-    vc = torch.zeros((1, 4, 256, L), device=dev, dtype=torch.bfloat16)
+    vc = torch.zeros((1, 4, L // 32, 256, 32), device=dev, dtype=torch.bfloat16)
     cu = torch.tensor([0, 700], device=dev, dtype=torch.int32)
     gdr.attn_prefill(q[:700], k[:700], v[:700], g[:700], qw, kw, cu, k_cache=kc, v_cache=vc)
     outs = []
@@ -208,7 +209,7 @@ def test_decode_full_size_sampled():
     say("attention decode full size N=64 L=32768")
     gen = torch.Generator(device=dev).manual_seed(49)
     kc = torch.randn((N, L, 4, 256), device=dev, generator=gen).to(torch.bfloat16)
-    vc = torch.randn((N, 4, 256, L), device=dev, generator=gen).to(torch.bfloat16)
+    vc = torch.randn((N, 4, L // 32, 256, 32), device=dev, generator=gen).to(torch.bfloat16)
     x = synth.attn_inputs(50, lengths=(1,) * N)
     q, k, v, g, qw, kw, _ = _dev(x, dev)
     lens = np.asarray(synth.rng(51).integers(32000, L, size=N), dtype=np.int32)
@@ -219,7 +220,7 @@ def test_decode_full_size_sampled():
         p = int(lens[n])
         qg, _ = _gpu_qrot_at(q[n], k[n], qw, kw, p, dev)
         kn = to_host(kc[n:n + 1, :p + 1])
-        vn = to_host(vc[n:n + 1, :, :, :p + 1]).transpose(0, 3, 1, 2)
+        vn = v_cache_natural(to_host(vc[n:n + 1]))[:, :p + 1]
         r = aref.core_decode(to_host(qg)[None], x.gate[n:n + 1], kn, vn, np.array([p + 1]))
         _check_out(to_host(out[n:n + 1]), r["out"], r["mass"])
 
@@ -254,12 +255,12 @@ def test_decode_full_cache():
     x = synth.attn_inputs(55, lengths=(1,) * N, hq=hq, hk=hk)
     rng = synth.rng(56)
     kc0 = synth.round_bf16(rng.standard_normal((N, L, hk, 256)))
-    vc0 = synth.round_bf16(rng.standard_normal((N, hk, 256, L)))
+    vc0 = synth.round_bf16(rng.standard_normal((N, L, hk, 256)))  # natural order
     say("attention decode at the last cache slot")
     q, k, v, g, qw, kw, _ = _dev(x, dev)
-    kc, vc = to_dev(kc0, "bf16", dev), to_dev(vc0, "bf16", dev)
+    kc, vc = to_dev(kc0, "bf16", dev), to_dev(v_cache_blocked(vc0), "bf16", dev)
     out = gdr.attn_decode(q, k, v, g, qw, kw, kc, vc, torch.tensor(lens, device=dev, dtype=torch.int32))
     torch.cuda.synchronize()
     qrot = np.stack([to_host(_gpu_qrot_at(q[n], k[n], qw, kw, p, dev)[0]) for n, p in enumerate(lens)])
-    r = aref.core_decode(qrot, x.gate, to_host(kc), to_host(vc).transpose(0, 3, 1, 2), np.asarray(lens) + 1)
+    r = aref.core_decode(qrot, x.gate, to_host(kc), v_cache_natural(to_host(vc)), np.asarray(lens) + 1)
     _check_out(to_host(out), r["out"], r["mass"])
