@@ -100,7 +100,7 @@ struct AttnArgs {
   const int32_t* cu_seqlens;       // prefill [N+1]
   const int32_t* cache_lens;       // decode [N]: cached tokens before this one
   void* out;                       // [rows, Hq, 256] bf16
-  void *k_cache, *v_cache;         // [N, cache_len, Hk, 256] and [N, Hk, 256, cache_len] bf16, or NULL (prefill)
+  void *k_cache, *v_cache;         // [N, cache_len, Hk, 256] and [N, Hk, cache_len/32, 256, 32] bf16, or NULL (prefill)
   int cache_len;
   int T, N, Hq, Hk;                // T: packed tokens (prefill) or N (decode)
   float eps;

@@ -14,11 +14,13 @@
 //
 // Two kernels.  The part that does not depend on the state -- Gram matrices,
 // q/k norms, decays, T and P -- is computed by chunk_prep_kernel, one
-// workgroup per (chunk, value head), all chunks of all sequences in parallel,
-// into a caller-provided workspace.  chunk_rec_kernel then carries the state:
-// one workgroup of 4 waves per (sequence, value head, 64 value channels),
-// wave w owning 16 value channels for the whole sequence, chunk after chunk:
-// X = K S0^T, R, Delta = T R, O, S update.  The matrix-core output layout
+// workgroup per (chunk, key head) serving the key head's value heads in
+// turn, all chunks of all sequences in parallel, into a caller-provided
+// workspace.  chunk_rec_kernel then carries the state: one workgroup per
+// (sequence, value head, 32 value channels), two state waves owning 16
+// value channels each for the whole sequence, chunk after chunk:
+// X = K S0^T, R, Delta = T R, S update; two output waves form O and two load
+// waves stage the inputs (see chunk_rec_kernel).  The matrix-core output layout
 // (lane l holds rows 4*(l/16)+i of column l%16) is fed back as the B operand
 // of the next contraction by permuting the contraction index identically on
 // both operands, so R, Delta and the state stay in registers; the shared A
