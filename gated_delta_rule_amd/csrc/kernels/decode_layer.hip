@@ -11,14 +11,19 @@
 // so it updates their conv state in place without racing another workgroup.
 //
 //   phase 0  each thread loads its conv channel's inputs and (threads
-//            0 .. G-1) the gate inputs, then every lane issues its 16 state
-//            loads (non-temporal), as in the decode kernel: waves 4g .. 4g+3
-//            stream value head kh*G + g, 32 rows each, 8 lanes per row
+//            0 .. G-1) the gate inputs, then every lane issues the state
+//            loads of its first two row steps (non-temporal): waves
+//            4g .. 4g+3 stream value head kh*G + g, 32 rows each, 8 lanes
+//            per row
 //   phase 1  conv + SiLU of the (2 + G) * 128 channels under the front's
 //            bit-exact contract (same code as the prefill front), the
 //            conv state rolled by one token, the gates; results to LDS
 //   phase 2  the state update and o, with the decode kernel's arithmetic and
-//            reduction order (so o and S match gdr_recurrent_step bit for bit)
+//            reduction order (so o and S match gdr_recurrent_step bit for bit),
+//            in two passes of two row steps: as the first pass writes a row
+//            back, the registers it held load the matching second-pass row,
+//            so those loads stream under the first pass's arithmetic and
+//            stores
 //   phase 3  the gated RMS norm of each value head's 128 outputs
 //
 // Bound by the state traffic like the decode step; the front and back add
@@ -97,9 +102,10 @@ __global__ __launch_bounds__(256 * G) void decode_layer_kernel(LayerStepArgs a) 
   const float gA = a.A_log[gh_ld], gdt = a.dt_bias[gh_ld];
   const int row0 = wh * (D / 4) + sub;
   float* S = a.state + ((size_t)slot * a.Hv + h) * D * D;
-  f32x4 s[NS][F4];
+  constexpr int NH = NS / 2;  // rows per pass
+  f32x4 s[NH][F4];
 #pragma unroll
-  for (int i = 0; i < NS; ++i)
+  for (int i = 0; i < NH; ++i)
 #pragma unroll
     for (int j = 0; j < F4; ++j)
       s[i][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(row0 + 8 * i) * D + 32 * j + 4 * e8));
@@ -165,9 +171,13 @@ __global__ __launch_bounds__(256 * G) void decode_layer_kernel(LayerStepArgs a) 
   kq *= rk * rq;
   const float alpha = expf(gl[gh]);
   const float b = bl[gh];
+  // two passes of NH row steps; as pass 0 frees a row's registers, the
+  // matching pass-1 row is loaded into them
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int r = row0 + 8 * i;
+  for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+  for (int i = 0; i < NH; ++i) {
+    const int r = row0 + 8 * (i + NH * pass);
     float pu = 0.f, pw = 0.f;
 #pragma unroll
     for (int j = 0; j < F4; ++j)
@@ -190,6 +200,12 @@ __global__ __launch_bounds__(256 * G) void decode_layer_kernel(LayerStepArgs a) 
 #pragma unroll
       for (int e = 0; e < 4; ++e) ns[e] = alpha * s[i][j][e] + delta * kv[j][e];
       __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + (size_t)r * D + 32 * j + 4 * e8));
+    }
+    if (pass == 0) {
+#pragma unroll
+      for (int j = 0; j < F4; ++j)
+        s[i][j] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4*>(S + (size_t)(r + 8 * NH) * D + 32 * j + 4 * e8));
     }
   }
   lds_sync();
