@@ -88,6 +88,31 @@ def test_prefill_against_oracle(lengths, hq, hk):
         assert not torch.any(kc[n, b - a:].float() != 0) and not torch.any(vn[n, b - a:].float() != 0)
 
 
+def test_prefill_sequence_longer_than_cache():
+    """A 200-token and a 70-token sequence into 128-slot caches: positions
+    below 128 receive k' and v (the blocked V cache through its converter),
+    the 70-token sequence leaves its tail slots untouched, and the output
+    does not depend on the cache."""
+    import gated_delta_rule_amd as gdr
+    import torch
+    dev = gpu()
+    lengths, L, hk = (200, 70), 128, 2
+    x = synth.attn_inputs(57, lengths=lengths, hq=6, hk=hk)
+    say(f"attention prefill lengths {lengths} into {L}-slot caches")
+    q, k, v, g, qw, kw, cu = _dev(x, dev)
+    kc = torch.full((2, L, hk, 256), 7.0, device=dev, dtype=torch.bfloat16)
+    vc = torch.full((2, hk, L // 32, 256, 32), 7.0, device=dev, dtype=torch.bfloat16)
+    out = gdr.attn_prefill(q, k, v, g, qw, kw, cu, k_cache=kc, v_cache=vc)
+    ref_out = gdr.attn_prefill(q, k, v, g, qw, kw, cu)
+    _, ko = gdr.attn_qk_norm_rope(q, k, qw, kw, cu)
+    torch.cuda.synchronize()
+    assert bits_equal(out, ref_out)
+    vn = v_cache_natural(vc)
+    assert bits_equal(kc[0], ko[:L]) and bits_equal(vn[0], v[:L])
+    assert bits_equal(kc[1, :70], ko[200:270]) and bits_equal(vn[1, :70], v[200:270])
+    assert torch.all(kc[1, 70:].float() == 7.0) and torch.all(vn[1, 70:].float() == 7.0)
+
+
 def test_prefill_full_size_sampled():
     """One 32768-token sequence at the layer's head shape: 24 sampled query
     rows (tile edges, the last row) on 6 heads against the oracle."""
