@@ -238,8 +238,9 @@ __global__ __launch_bounds__(1024) void chunk_table_kernel(const int32_t* cu, in
 // Chunk preparation: T = (I + A)^{-1}, P and token factors of every value
 // head of one (chunk, key head).
 
-// LDS of chunk_prep_kernel (36 KiB, so four workgroups share a compute
-// unit): k and q rows are dead once the Gram tiles are in registers, so A and
+// LDS of chunk_prep_kernel (35 KiB plus 512 B per value head of the key
+// head, so four workgroups share a compute unit up to 8 value heads per key
+// head): k and q rows are dead once the Gram tiles are in registers, so A and
 // T reuse their space; the 16x16 and 32x32 products of the merges are staged
 // in A's never-used upper right 32x32 block (rows 0..31, columns 32..63).
 struct __align__(16) PrepSmem {
@@ -252,9 +253,8 @@ struct __align__(16) PrepSmem {
     float Tf[kC][kC + 4];
   };
   float ssk[kC], ssq[kC];
-  float G2[kC], rk[kC], ar[kC], pr[kC];
-  float bin[kC];
-};
+  float rk[kC], pr[kC];
+};  // followed in LDS by the per-head log2 decays and beta r_k, [G][64] each
 static_assert(sizeof(PrepSmem) <= 40 * 1024, "four prepare workgroups per compute unit");
 
 __global__ __launch_bounds__(kNT, 4) void chunk_prep_kernel(ChunkArgs a, unsigned char* ws) {
@@ -275,11 +275,13 @@ __global__ __launch_bounds__(kNT, 4) void chunk_prep_kernel(ChunkArgs a, unsigne
   const ChunkPos pos = locate_chunk(a, table, j);
   if (!pos.valid) return;
   const int c0 = pos.c0, L = pos.L;
-  // g (wave 0) or beta (wave 1) of token `lane` of value head kh*G + hh
-  auto load_gb = [&](int hh) {
-    return (wave < 2 && lane < L) ? (wave == 0 ? a.g : a.beta)[(size_t)(c0 + lane) * a.Hv + kh * G + hh] : 0.f;
-  };
-  float gnext = load_gb(0);
+  // g and beta of token `lane` of value head kh*G + hh (zero past L)
+  auto load_g = [&](int hh) { return lane < L ? a.g[(size_t)(c0 + lane) * a.Hv + kh * G + hh] : 0.f; };
+  auto load_b = [&](int hh) { return lane < L ? a.beta[(size_t)(c0 + lane) * a.Hv + kh * G + hh] : 0.f; };
+  // wave w's first head (w) now, so the loads run under the k/q loads and the Gram tiles
+  const float g_first = wave < G ? load_g(wave) : 0.f, b_first = wave < G ? load_b(wave) : 0.f;
+  float* G2h = reinterpret_cast<float*>(smem_raw + sizeof(PrepSmem));  // [G][64] log2 decays
+  float* arh = G2h + G * kC;                                             // [G][64] beta r_k
 
   // ---- k, q rows to LDS with permuted columns
   {
@@ -340,51 +342,53 @@ __global__ __launch_bounds__(kNT, 4) void chunk_prep_kernel(ChunkArgs a, unsigne
   }
   lds_barrier();
 
+  // ---- decays and factors of every value head, wave w taking heads w, w + 4, ...
+  {
+    const float rkv = a.use_l2 ? 1.f / sqrtf(sm.ssk[lane] + a.eps) : 1.f;
+    const float rqv = a.use_l2 ? 1.f / sqrtf(sm.ssq[lane] + a.eps) : 1.f;
+    if (wave == 0) {
+      sm.rk[lane] = rkv;
+      sm.pr[lane] = a.scale * rqv;
+    }
+    for (int hh = wave; hh < G; hh += kNT / 64) {
+      float gv = hh == wave ? g_first : load_g(hh);
+      const float bv = hh == wave ? b_first : load_b(hh);
+      gv = gv < kMinLogDecay ? kMinLogDecay : gv;  // (a NaN stays NaN)
+      // chunk-local cumulative log-decay, summed in fp64; kept as log2 (G * log2 e)
+      double Gs = (double)gv;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(Gs, off, 64);
+        if (lane >= off) Gs += o;
+      }
+      const float g2 = (float)(Gs * 1.4426950408889634);
+      const float g2L = __shfl(g2, 63, 64);
+      const float eG = exp2f(g2);
+      G2h[hh * kC + lane] = g2;
+      arh[hh * kC + lane] = bv * rkv;
+      float* facg = reinterpret_cast<float*>(ws + kTableBytes(a.N) + ((size_t)j * a.Hv + kh * G + hh) * kRecBytes +
+                                             kFacOff);
+      facg[lane] = bv;                           // bt
+      facg[64 + lane] = bv * eG * rkv;           // xr
+      facg[128 + lane] = a.scale * rqv * eG;     // yq
+      facg[192 + lane] = rkv * exp2f(g2L - g2);  // cL
+      if (lane == 0) facg[256] = exp2f(g2L);     // e^{G_L}
+    }
+  }
+  lds_barrier();
+
   for (int hh = 0; hh < G; ++hh) {
     const int h = kh * G + hh;
+    const float* G2 = G2h + hh * kC;
+    const float* ar = arh + hh * kC;
+    // every wave is done with the previous head's T (split below) before
+    // this head rewrites A and T
+    if (hh > 0) lds_barrier();
     unsigned char* rec = ws + kTableBytes(a.N) + ((size_t)j * a.Hv + h) * kRecBytes;
     uint16_t* Thg = reinterpret_cast<uint16_t*>(rec);
     uint16_t* Tlg = reinterpret_cast<uint16_t*>(rec + kMatBytes);
     uint16_t* Phg = reinterpret_cast<uint16_t*>(rec + 2 * kMatBytes);
     uint16_t* Plg = reinterpret_cast<uint16_t*>(rec + 3 * kMatBytes);
-    float* facg = reinterpret_cast<float*>(rec + kFacOff);
-    {
-      float gv = gnext;
-      if (hh + 1 < G) gnext = load_gb(hh + 1);  // the next head's, a whole head ahead
-      if (wave == 1) sm.bin[lane] = gv;
-      if (wave == 0) {
-        gv = gv < kMinLogDecay ? kMinLogDecay : gv;  // (a NaN stays NaN)
-        // chunk-local cumulative log-decay, summed in fp64; kept as log2 (G * log2 e)
-        double Gs = (double)gv;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const double o = __shfl_up(Gs, off, 64);
-          if (lane >= off) Gs += o;
-        }
-        sm.G2[lane] = (float)(Gs * 1.4426950408889634);
-      }
-    }
-    lds_barrier();
-
-    // ---- per-token factors (wave 0): norms and scales
-    if (wave == 0) {
-      const float rkv = a.use_l2 ? 1.f / sqrtf(sm.ssk[lane] + a.eps) : 1.f;
-      const float rqv = a.use_l2 ? 1.f / sqrtf(sm.ssq[lane] + a.eps) : 1.f;
-      const float g2 = sm.G2[lane];
-      const float g2L = sm.G2[63];
-      const float eG = exp2f(g2);
-      const float bv = sm.bin[lane];
-      sm.rk[lane] = rkv;
-      sm.ar[lane] = bv * rkv;
-      sm.pr[lane] = a.scale * rqv;
-      facg[lane] = bv;                         // bt
-      facg[64 + lane] = bv * eG * rkv;         // xr
-      facg[128 + lane] = a.scale * rqv * eG;   // yq
-      facg[192 + lane] = rkv * exp2f(g2L - g2);  // cL
-      if (lane == 0) facg[256] = exp2f(g2L);   // e^{G_L}
-    }
-    lds_barrier();
-
     // ---- scale Gram tiles into A (fp32, LDS) and P (hi/lo bf16, workspace)
 #pragma unroll
     for (int u = 0; u < 5; ++u) {
@@ -392,10 +396,10 @@ __global__ __launch_bounds__(kNT, 4) void chunk_prep_kernel(ChunkArgs a, unsigne
       if (job >= 20) break;
       const int ti = gti[u], tj = gtj[u];
       const int i = 16 * ti + c, j0 = 16 * tj + 4 * q4;
-      const float g2i = sm.G2[i];
-      const f32x4 g2j = *reinterpret_cast<const f32x4*>(&sm.G2[j0]);
+      const float g2i = G2[i];
+      const f32x4 g2j = *reinterpret_cast<const f32x4*>(&G2[j0]);
       const f32x4 rkj = *reinterpret_cast<const f32x4*>(&sm.rk[j0]);
-      const float rowf = job < 10 ? sm.ar[i] : sm.pr[i];
+      const float rowf = job < 10 ? ar[i] : sm.pr[i];
       f32x4 val;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1042,7 +1046,7 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, void* workspace, hipStream_t st
   }
   const size_t nch = max_chunks(a);
   if (nch > 0) {
-    const size_t smem = sizeof(PrepSmem);
+    const size_t smem = sizeof(PrepSmem) + 2 * (size_t)(a.Hv / a.Hk) * kC * sizeof(float);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_prep_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
