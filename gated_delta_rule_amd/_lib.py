@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
 GDR_OK, GDR_ERR_INVALID_ARG, GDR_ERR_UNSUPPORTED, GDR_ERR_HIP = 0, -1, -2, -3
 GDR_F32, GDR_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 64 << 20  # GDR_NOALLOC_SCRATCH_BYTES
 
 EXPORTED = (
     "gdr_abi_version",
@@ -22,6 +23,7 @@ EXPORTED = (
     "gdr_chunk_fwd",
     "gdr_chunk_fwd_prepare",
     "gdr_chunk_fwd_recurrence",
+    "gdr_chunk_fwd_noalloc",
     "gdr_recurrent_step",
     "gdr_recurrent_step_indexed",
     "gdr_decode_layer_step",
@@ -152,6 +154,8 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = I32
         fn.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, P, P, P, P, SZ, P]
+    lib.gdr_chunk_fwd_noalloc.restype = I32
+    lib.gdr_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, P, P, P, P]
     lib.gdr_recurrent_step.restype = I32
     lib.gdr_recurrent_step.argtypes = [ctypes.POINTER(GdrDesc), P, P, P, P, P, P, P, P]
     lib.gdr_recurrent_step_indexed.restype = I32

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "internal.h"
@@ -79,6 +80,36 @@ gdr_status check_desc(const gdr_desc* d, bool decode, bool has_cu) {
   return GDR_OK;
 }
 
+}  // namespace
+
+// Static device scratch of gdr_chunk_fwd_noalloc: the workspace of callers
+// that cannot allocate.  Every GPU the library runs on holds its own copy
+// for the life of the process.  In host code `scratch` names a host-side
+// stand-in, so kernels only ever get the device address that
+// hipGetSymbolAddress returns for the current device.
+namespace {
+__device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+gdr_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GDR_ERR_UNSUPPORTED, "device %d: the scratch table covers devices 0..%d", dev, kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(GDR_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDR_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -194,6 +225,28 @@ gdr_status gdr_chunk_fwd_recurrence(const gdr_desc* d, const void* q, const void
                                     size_t workspace_bytes, void* stream) {
   return chunk_fwd(d, q, k, v, g, beta, initial_state, final_state, cu_seqlens, o, workspace, workspace_bytes,
                    stream, gdr::kStageRecur, "gdr_chunk_fwd_recurrence launch");
+}
+
+
+gdr_status gdr_chunk_fwd_noalloc(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* initial_state, float* final_state,
+                                 const int32_t* cu_seqlens, void* o, void* stream) {
+  gdr_status st = check_desc(d, false, cu_seqlens != nullptr);
+  if (st != GDR_OK) return st;
+  const size_t need = workspace_bytes_for(d);
+  if (need > (size_t)GDR_NOALLOC_SCRATCH_BYTES)
+    return fail(GDR_ERR_INVALID_ARG,
+                "gdr_chunk_fwd_noalloc: this call needs %zu bytes of workspace, the static scratch holds %zu "
+                "(use gdr_chunk_fwd with a caller workspace)",
+                need, (size_t)GDR_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_of_current_device(&ws);
+    if (st != GDR_OK) return st;
+  }
+  return chunk_fwd(d, q, k, v, g, beta, initial_state, final_state, cu_seqlens, o, ws,
+                   need > 0 ? (size_t)GDR_NOALLOC_SCRATCH_BYTES : 0, stream, gdr::kStagePrepare | gdr::kStageRecur,
+                   "gdr_chunk_fwd_noalloc launch");
 }
 
 static gdr_status recurrent_step(const gdr_desc* d, const void* q, const void* k, const void* v, const float* g,

@@ -143,6 +143,31 @@ gdr_status gdr_chunk_fwd(const gdr_desc* d, const void* q, const void* k, const 
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gdr_chunk_fwd without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of gdr_chunk_fwd; the kernels are the same, so the outputs are bit for bit
+ * those of gdr_chunk_fwd.  The workspace is a static device array of
+ * GDR_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load until the
+ * process ends; its address is looked up (hipGetSymbolAddress) on the first
+ * call made with that device current.  The call allocates and frees
+ * nothing.
+ *   INVALID_ARG  the call needs more workspace than the scratch holds
+ *                (gdr_chunk_fwd_workspace_size(d) > GDR_NOALLOC_SCRATCH_BYTES;
+ *                about 2 700 tokens at 48 value heads) -- nothing is enqueued
+ *   UNSUPPORTED  the current device index is 64 or more
+ * The calling thread's current device must be the device of `stream`.  All
+ * calls on one GPU share its scratch and it keeps the last call's contents:
+ * two calls that can run at the same time on one GPU (different streams, or
+ * different threads) race and give undefined results.  Nothing in the
+ * scratch needs to start at zero.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES (64u << 20)
+gdr_status gdr_chunk_fwd_noalloc(const gdr_desc* d, const void* q, const void* k, const void* v,
+                                 const float* g, const float* beta, const float* initial_state,
+                                 float* final_state, const int32_t* cu_seqlens, void* o, void* stream);
+
+/*
  * The two stages of gdr_chunk_fwd, for callers that time or schedule them
  * apart.  Arguments, checks and errors are those of gdr_chunk_fwd, and
  * gdr_chunk_fwd_prepare followed by gdr_chunk_fwd_recurrence on one stream

@@ -280,3 +280,20 @@ def test_no_oracle_in_product_path():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", src, flags=re.M), f
                 assert "oracle/" not in src and "oracle." not in src, f
+
+
+def test_chunk_fwd_noalloc_rejects_calls_beyond_the_scratch():
+    """A call whose workspace exceeds the static scratch fails before any
+    HIP call (no device is touched on this CPU-only host)."""
+    lib = _lib.load()
+    d = _desc(seq_len=1 << 20)
+    nbytes = ctypes.c_size_t(0)
+    assert lib.gdr_chunk_fwd_workspace_size(ctypes.byref(d), ctypes.byref(nbytes)) == 0
+    assert nbytes.value > _lib.NOALLOC_SCRATCH_BYTES
+    st = lib.gdr_chunk_fwd_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None)
+    assert st == -1
+    assert "static scratch" in lib.gdr_last_error().decode()
+    # bad descriptors are rejected as gdr_chunk_fwd rejects them
+    st = lib.gdr_chunk_fwd_noalloc(ctypes.byref(_desc(num_v_heads=40)), FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                   None, FAKE, None)
+    assert st == -1 and "multiple" in lib.gdr_last_error().decode()
