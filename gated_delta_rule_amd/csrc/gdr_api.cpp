@@ -139,6 +139,7 @@ static size_t workspace_bytes_for(const gdr_desc* d) {
   gdr::ChunkArgs a{};
   a.N = d->num_seqs;
   a.T = d->seq_len;
+  a.Hk = d->num_k_heads;
   a.Hv = d->num_v_heads;
   // With batch == 1 the same descriptor may describe a packed batch, whose
   // chunk count is bounded by ceil(T/64) + N; size for that bound.
