@@ -92,7 +92,7 @@ def long_context_host(n: int = N_CALLS):
     """The n calls' host inputs, generated in parallel threads (numpy releases
     the GIL in the heavy parts)."""
     import concurrent.futures as cf
-    from gated_delta_rule_amd import synth
+    from inputs import synth
     workers = max(1, min(n, len(os.sched_getaffinity(0)) // 2))
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
         return list(ex.map(lambda i: synth.long_context_call(i, T=T_CALL), range(n)))
@@ -202,7 +202,7 @@ def bench_decode(steps: int = 256, replicas: int = 1, pool: int = 0):
     slots (gdr_recurrent_step_indexed) with the rows naming shuffled slots."""
     import torch
     import gated_delta_rule_amd as gdr
-    from gated_delta_rule_amd import synth
+    from inputs import synth
     dev = torch.device("cuda:0")
     N = 64
     log(f"decode: N={N}, {steps} steps, " + (f"pool of {pool} slots" if pool else f"{replicas} state replica(s)"))
@@ -250,7 +250,7 @@ def bench_decode_layer(steps: int = 128):
     plus x, the conv state (read and written), a, b, z and y."""
     import torch
     import gated_delta_rule_amd as gdr
-    from gated_delta_rule_amd import synth
+    from inputs import synth
     dev = torch.device("cuda:0")
     N = 64
     C = (2 * HK + HV) * D
@@ -308,7 +308,7 @@ def bench_decode_layer(steps: int = 128):
 def bench_pipeline(reps: int = 5):
     import torch
     import gated_delta_rule_amd as gdr
-    from gated_delta_rule_amd import synth
+    from inputs import synth
     dev = torch.device("cuda:0")
     log("pipeline: generating 8-sequence packed batch (65536 tokens)")
     p = synth.pipeline_inputs()
@@ -353,7 +353,7 @@ def bench_layer(reps: int = 5):
     on the same operands (hipBLASLt) is timed beside them as a reference."""
     import torch
     import gated_delta_rule_amd as gdr
-    from gated_delta_rule_amd import synth
+    from inputs import synth
     dev = torch.device("cuda:0")
     T, H = T_CALL, synth.HIDDEN
     Cq, V = (2 * HK + HV) * D, HV * D
@@ -444,7 +444,7 @@ def bench_attention(reps: int = 3, dec_steps: int = 20):
     filled to 32 000+ tokens, as KV-cache bytes read per step against HBM."""
     import torch
     import gated_delta_rule_amd as gdr
-    from gated_delta_rule_amd import synth
+    from inputs import synth
     dev = torch.device("cuda:0")
     Hq, Hk, Da = synth.ATTN_HQ, synth.ATTN_HK, synth.ATTN_D
     T = T_CALL
@@ -557,7 +557,7 @@ def cpu_baseline_decode(steps: int = 4, N: int = 64):
     """The fp64 oracle's decode step on the decode workload (64 sequences x 48
     heads, 128x128 state), 4 steps, sequences spread over the host's cores."""
     import multiprocessing as mp
-    from gated_delta_rule_amd import synth
+    from inputs import synth
     procs = min(len(os.sched_getaffinity(0)), N)
     _, _, s0 = synth.decode_inputs(N=N)
     xs = [synth.decode_step_inputs(t, N=N) for t in range(steps)]

@@ -16,7 +16,7 @@ Tolerances (derived from the arithmetic):
 import numpy as np
 import pytest
 
-from gated_delta_rule_amd import synth
+from inputs import synth
 from oracle import attention as aref
 from helpers import bf16_ulp, bits_equal, gpu, say, to_dev, to_host, v_cache_blocked, v_cache_natural
 

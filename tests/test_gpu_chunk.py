@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from gated_delta_rule_amd import synth
+from inputs import synth
 from oracle import gdr as ref
 from helpers import BF16_TOL, F32_TOL, bits_equal, gpu, rel_err, say, to_dev, to_host
 

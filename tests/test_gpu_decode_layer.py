@@ -3,7 +3,7 @@ path in one launch) against the fp64 oracle, and against the unfused kernels."""
 import numpy as np
 import pytest
 
-from gated_delta_rule_amd import synth
+from inputs import synth
 from oracle import conv as cref
 from oracle import gdr as ref
 from helpers import BF16_TOL, bf16_ulp, bits_equal, gpu, rel_err, say, to_dev, to_host

@@ -3,7 +3,7 @@ and the whole delta-layer path checked stage by stage."""
 import numpy as np
 import pytest
 
-from gated_delta_rule_amd import synth
+from inputs import synth
 from oracle import conv as cref
 from oracle import gdr as ref
 from helpers import BF16_TOL, bf16_ulp, gpu, rel_err, say, to_dev, to_host

@@ -10,7 +10,7 @@ ulp of the result.
 import numpy as np
 import pytest
 
-from gated_delta_rule_amd import synth
+from inputs import synth
 from oracle import conv as cref
 from oracle import gdr as gref
 from oracle import layer as lref

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 from oracle import conv
-from gated_delta_rule_amd import synth
+from inputs import synth
 
 
 def _bf16_ulp(x):

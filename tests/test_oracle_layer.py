@@ -5,7 +5,7 @@ from fractions import Fraction
 
 import numpy as np
 
-from gated_delta_rule_amd import synth
+from inputs import synth
 from oracle import conv as cv
 from oracle import gdr
 from oracle import layer

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 from oracle import gdr
-from gated_delta_rule_amd import synth
+from inputs import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 

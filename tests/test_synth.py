@@ -1,7 +1,7 @@
 """Seeded generators: deterministic, right shapes and distributions (CPU only)."""
 import numpy as np
 
-from gated_delta_rule_amd import synth
+from inputs import synth
 
 
 def test_deterministic():

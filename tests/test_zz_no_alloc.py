@@ -25,7 +25,8 @@ def _call_noalloc(desc, q, k, v, g, beta, init, fin, cu, o):
 def test_noalloc_matches_workspace_call(out_dtype):
     import torch
     import gated_delta_rule_amd as gdr_amd
-    from gated_delta_rule_amd import ops, synth
+    from gated_delta_rule_amd import ops
+    from inputs import synth
     dev = gpu()
     odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
     cases = [
