@@ -8,9 +8,13 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
+#include "host_checks.h"
 #include "internal.h"
 
 namespace {
@@ -77,6 +81,66 @@ gdr_status check_desc(const gdr_desc* d, bool decode, bool has_cu) {
   const double tokens = (double)d->batch * d->seq_len;
   if (tokens * d->num_v_heads * d->head_dim_v >= 9.0e18)
     return fail(GDR_ERR_INVALID_ARG, "problem too large");
+  return GDR_OK;
+}
+
+
+// GDR_DEBUG_CHECKS (read at every call; unset, empty or "0" = off): the index
+// arrays the kernels trust are copied to the host and checked, and workspaces
+// are filled with NaN bytes before the kernels run, so a read of a workspace
+// entry that no kernel wrote shows up in the results.  The copies wait for
+// the stream; the mode is for debugging, not for graph capture.
+bool debug_checks() {
+  const char* e = std::getenv("GDR_DEBUG_CHECKS");
+  return e && *e && std::strcmp(e, "0") != 0;
+}
+
+gdr_status debug_read_i32(const int32_t* p, size_t n, hipStream_t s, std::vector<int32_t>* out, const char* what) {
+  out->assign(n, 0);
+  if (n == 0) return GDR_OK;
+  hipError_t e = hipMemcpyAsync(out->data(), p, n * sizeof(int32_t), hipMemcpyDefault, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(GDR_ERR_HIP, "GDR_DEBUG_CHECKS: reading %s: %s", what, hipGetErrorString(e));
+  return GDR_OK;
+}
+
+gdr_status debug_check_cu(const int32_t* cu, int N, long long tokens, void* stream, const char* what) {
+  if (!cu || !debug_checks()) return GDR_OK;
+  std::vector<int32_t> h;
+  gdr_status st = debug_read_i32(cu, (size_t)N + 1, static_cast<hipStream_t>(stream), &h, what);
+  if (st != GDR_OK) return st;
+  char msg[256];
+  if (!gdr::check_cu_seqlens(h.data(), N, tokens, what, msg, sizeof msg))
+    return fail(GDR_ERR_INVALID_ARG, "GDR_DEBUG_CHECKS: %s", msg);
+  return GDR_OK;
+}
+
+gdr_status debug_check_indices(const int32_t* idx, int N, int pool, void* stream) {
+  if (!idx || !debug_checks()) return GDR_OK;
+  std::vector<int32_t> h;
+  gdr_status st = debug_read_i32(idx, (size_t)N, static_cast<hipStream_t>(stream), &h, "state_indices");
+  if (st != GDR_OK) return st;
+  char msg[256];
+  if (!gdr::check_state_indices(h.data(), N, pool, msg, sizeof msg))
+    return fail(GDR_ERR_INVALID_ARG, "GDR_DEBUG_CHECKS: %s", msg);
+  return GDR_OK;
+}
+
+gdr_status debug_check_cache_lens(const int32_t* lens, int N, int cache_len, void* stream) {
+  if (!lens || !debug_checks()) return GDR_OK;
+  std::vector<int32_t> h;
+  gdr_status st = debug_read_i32(lens, (size_t)N, static_cast<hipStream_t>(stream), &h, "cache_lens");
+  if (st != GDR_OK) return st;
+  char msg[256];
+  if (!gdr::check_cache_lens(h.data(), N, cache_len, msg, sizeof msg))
+    return fail(GDR_ERR_INVALID_ARG, "GDR_DEBUG_CHECKS: %s", msg);
+  return GDR_OK;
+}
+
+gdr_status debug_poison(void* ws, size_t bytes, void* stream) {
+  if (!ws || !bytes || !debug_checks()) return GDR_OK;
+  hipError_t e = hipMemsetAsync(ws, 0xFF, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(GDR_ERR_HIP, "GDR_DEBUG_CHECKS: filling the workspace: %s", hipGetErrorString(e));
   return GDR_OK;
 }
 
@@ -176,6 +240,9 @@ static gdr_status chunk_fwd(const gdr_desc* d, const void* q, const void* k, con
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(GDR_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace ? workspace_bytes : 0);
   if (need > 0 && !aligned16(workspace)) return fail(GDR_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if ((st = debug_check_cu(cu_seqlens, d->num_seqs, d->seq_len, stream, "cu_seqlens")) != GDR_OK) return st;
+  // the recurrence stage alone reads what prepare left in the workspace
+  if ((stages & gdr::kStagePrepare) && (st = debug_poison(workspace, need, stream)) != GDR_OK) return st;
   gdr::ChunkArgs a{};
   a.q = q;
   a.k = k;
@@ -261,6 +328,7 @@ static gdr_status recurrent_step(const gdr_desc* d, const void* q, const void* k
   if (!q || !k || !v || !g || !beta || (!state && !empty_pool) || !o)
     return fail(GDR_ERR_INVALID_ARG, "q, k, v, g, beta, state and o are required");
   if (!aligned16(state)) return fail(GDR_ERR_INVALID_ARG, "state must be 16-byte aligned");
+  if ((st = debug_check_indices(state_indices, d->batch, pool_size, stream)) != GDR_OK) return st;
   gdr::DecodeArgs a{};
   a.q = q;
   a.k = k;
@@ -318,6 +386,7 @@ gdr_status gdr_decode_layer_step(const gdr_desc* d, const void* x, const void* c
     return fail(GDR_ERR_INVALID_ARG, "x, conv_w, conv_state, a, b, A_log, dt_bias, state, z, norm_w and y are required");
   if (!aligned16(state) || reinterpret_cast<uintptr_t>(conv_w) % 8)
     return fail(GDR_ERR_INVALID_ARG, "state must be 16-byte and conv_w 8-byte aligned");
+  if ((st = debug_check_indices(state_indices, d->batch, pool_size, stream)) != GDR_OK) return st;
   gdr::LayerStepArgs la{};
   la.x = x;
   la.conv_w = conv_w;
@@ -362,6 +431,8 @@ gdr_status gdr_conv_gate_fused(const gdr_conv_desc* d, const void* x, const void
     return fail(GDR_ERR_INVALID_ARG, "conv_state_out must not alias conv_state_in");
   if (!aligned16(x) || !aligned16(conv_w) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(v_out))
     return fail(GDR_ERR_INVALID_ARG, "x, conv_w and q/k/v outputs must be 16-byte aligned");
+  const gdr_status st = debug_check_cu(cu_seqlens, d->num_seqs, d->num_tokens, stream, "cu_seqlens");
+  if (st != GDR_OK) return st;
   gdr::ConvArgs c{};
   c.x = x;
   c.w = conv_w;
@@ -542,6 +613,8 @@ gdr_status gdr_delta_layer_fwd(const gdr_layer_desc* d, const void* hidden, cons
   if (!workspace || workspace_bytes < p.total)
     return fail(GDR_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", p.total, workspace ? workspace_bytes : 0);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GDR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if ((st = debug_check_cu(cu_seqlens, d->num_seqs, d->num_tokens, stream, "cu_seqlens")) != GDR_OK) return st;
+  if ((st = debug_poison(workspace, p.total, stream)) != GDR_OK) return st;
   const int T = d->num_tokens, H = d->hidden, Hk = d->num_k_heads, Hv = d->num_v_heads, D = d->head_dim;
   const int C = (2 * Hk + Hv) * D, V = Hv * D;
   unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -630,6 +703,7 @@ gdr_status gdr_attn_qk_norm_rope(const gdr_attn_desc* d, const void* q, const vo
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(q_norm_w) ||
       !aligned16(k_norm_w))
     return fail(GDR_ERR_INVALID_ARG, "tensors must be 16-byte aligned");
+  if ((st = debug_check_cu(cu_seqlens, d->num_seqs, d->num_tokens, stream, "cu_seqlens")) != GDR_OK) return st;
   gdr::AttnArgs a = attn_args(d);
   a.q = q;
   a.k = k;
@@ -667,6 +741,8 @@ gdr_status gdr_attn_prefill(const gdr_attn_desc* d, const void* q, const void* k
   if (!workspace || workspace_bytes < need)
     return fail(GDR_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace ? workspace_bytes : 0);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GDR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if ((st = debug_check_cu(cu_seqlens, d->num_seqs, d->num_tokens, stream, "cu_seqlens")) != GDR_OK) return st;
+  if ((st = debug_poison(workspace, need, stream)) != GDR_OK) return st;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -708,6 +784,8 @@ gdr_status gdr_attn_decode(const gdr_attn_desc* d, const void* q, const void* k,
   if (!workspace || workspace_bytes < need)
     return fail(GDR_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace ? workspace_bytes : 0);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GDR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if ((st = debug_check_cache_lens(cache_lens, d->num_seqs, d->cache_len, stream)) != GDR_OK) return st;
+  if ((st = debug_poison(workspace, need, stream)) != GDR_OK) return st;
   a.q = q;
   a.k = k;
   a.v = v;

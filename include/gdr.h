@@ -19,13 +19,26 @@
  *   - Tensor arguments are DEVICE pointers, owned by the caller, contiguous
  *     in the layout documented per argument and 16-byte aligned.  Descriptor
  *     and size arguments are HOST pointers.
- *   - The library allocates nothing, frees nothing and never synchronises:
+ *   - The library allocates nothing, frees nothing and never synchronises
+ *     (apart from the debug mode below and gdr_chunk_fwd_noalloc's static
+ *     scratch):
  *     every kernel is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) and the call returns immediately.
  *   - Argument errors are reported synchronously, before anything is
  *     enqueued, as a negative gdr_status; gdr_last_error() then returns a
  *     thread-local message.  Device-side faults surface at the caller's next
  *     synchronisation.  Device array CONTENTS (e.g. cu_seqlens) are trusted.
+ *   - Debug mode: with the environment variable GDR_DEBUG_CHECKS set (and not
+ *     "0"), read at every call, each entry point first copies the index
+ *     arrays it would trust to the host and checks them -- cu_seqlens
+ *     (cu[0] == 0, non-decreasing, cu[N] == the token count), state_indices
+ *     (no pool slot named twice), cache_lens (0 <= len < cache_len) -- and
+ *     returns GDR_ERR_INVALID_ARG naming the first bad entry; then it fills
+ *     its workspace with 0xFF bytes (NaN in fp32 and bf16) before the
+ *     kernels run, so that a read of a workspace entry no kernel wrote shows
+ *     up as NaN in the results.  The copies wait for `stream` to drain; a
+ *     failed copy returns GDR_ERR_HIP.  The mode is for debugging, not for
+ *     HIP graph capture.  Results are bit-identical with and without it.
  *   - Value head h reads key head h / (Hv / Hk) (contiguous groups).
  *   - Thread safety: calls from several host threads are safe; kernels that
  *     write the same output buffers concurrently race, as usual.

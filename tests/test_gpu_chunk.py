@@ -1,4 +1,6 @@
 """GPU parity of gdr_chunk_fwd (chunked prefill) against the fp64 oracle."""
+import functools
+
 import numpy as np
 import pytest
 
@@ -7,6 +9,12 @@ from oracle import gdr as ref
 from helpers import BF16_TOL, F32_TOL, bits_equal, gpu, rel_err, say, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
+
+
+@functools.lru_cache(maxsize=1)
+def _long_call(i):
+    """Inputs of call i of the 262 144-token sequence (drawing one takes ~20 s)."""
+    return synth.long_context_call(i)
 
 
 def _dev_inputs(x, dev, cu=None, s0=None):
@@ -297,7 +305,7 @@ def test_long_context_resume():
     import gated_delta_rule_amd as gdr_amd
     import torch
     dev = gpu()
-    x0 = synth.long_context_call(0)
+    x0 = _long_call(0)
     say("long context: call 0 prefix checks")
     a = _dev_inputs(x0, dev)
     o_full, _ = gdr_amd.chunk_gated_delta_rule(a["q"], a["k"], a["v"], a["g"], a["beta"])
@@ -331,3 +339,28 @@ def test_long_context_resume():
         norms.append(float(state.norm()))
     # beta <= 1 and unit keys bound every state row by max |v| / (1 - max alpha); no blow-up
     assert max(norms) < 1e3
+
+
+def test_long_context_chained_calls_against_oracle():
+    """CFG4 beyond the 16K prefix: two chained 32768-token calls (65 536
+    tokens, final_state -> initial_state), against the oracle carrying its own
+    fp64 state from call to call, on three sampled value heads: every output
+    of each call and the state after each call."""
+    import gated_delta_rule_amd as gdr_amd
+    import torch
+    dev = gpu()
+    heads = [1, 20, 46]
+    state = torch.zeros((1, 48, 128, 128), device=dev)
+    s_ref = np.zeros((1, 48, 128, 128))
+    for i in range(2):
+        say(f"long context: chained call {i} against the oracle, heads {heads}")
+        xi = _long_call(i)
+        ai = _dev_inputs(xi, dev)
+        o, _ = gdr_amd.chunk_gated_delta_rule(ai["q"], ai["k"], ai["v"], ai["g"], ai["beta"], state,
+                                              final_state=state)
+        o_ref, s_ref = ref.forward(xi.q, xi.k, xi.v, xi.g, xi.beta, s_ref, heads=heads)
+        torch.cuda.synchronize()
+        oh = to_host(o[:, :, heads])
+        sh = to_host(state[:, heads])
+        assert rel_err(oh, o_ref[:, :, heads]) <= BF16_TOL, f"call {i}: o"
+        assert rel_err(sh, s_ref[:, heads]) <= BF16_TOL, f"call {i}: state"
