@@ -72,6 +72,11 @@ gdr_status check_desc(const gdr_desc* d, bool decode, bool has_cu) {
   } else {
     if (d->chunk_size != 64 && d->chunk_size != 32)
       return fail(GDR_ERR_UNSUPPORTED, "chunk_size %d: need 32 or 64", d->chunk_size);
+    // the bf16-MFMA path (bf16, d = 128, chunk 64) bounds the value heads per key head
+    if (d->qkv_dtype == GDR_BF16 && d->head_dim_k == 128 && d->chunk_size == 64 &&
+        d->num_v_heads / d->num_k_heads > gdr::kChunkMaxHeadRatio)
+      return fail(GDR_ERR_UNSUPPORTED, "bf16 prefill supports up to %d value heads per key head (got %d)",
+                  gdr::kChunkMaxHeadRatio, d->num_v_heads / d->num_k_heads);
     if (has_cu) {
       if (d->batch != 1) return fail(GDR_ERR_INVALID_ARG, "cu_seqlens needs batch == 1");
     } else if (d->num_seqs != d->batch) {
@@ -122,17 +127,6 @@ gdr_status debug_check_indices(const int32_t* idx, int N, int pool, void* stream
   if (st != GDR_OK) return st;
   char msg[256];
   if (!gdr::check_state_indices(h.data(), N, pool, msg, sizeof msg))
-    return fail(GDR_ERR_INVALID_ARG, "GDR_DEBUG_CHECKS: %s", msg);
-  return GDR_OK;
-}
-
-gdr_status debug_check_cache_lens(const int32_t* lens, int N, int cache_len, void* stream) {
-  if (!lens || !debug_checks()) return GDR_OK;
-  std::vector<int32_t> h;
-  gdr_status st = debug_read_i32(lens, (size_t)N, static_cast<hipStream_t>(stream), &h, "cache_lens");
-  if (st != GDR_OK) return st;
-  char msg[256];
-  if (!gdr::check_cache_lens(h.data(), N, cache_len, msg, sizeof msg))
     return fail(GDR_ERR_INVALID_ARG, "GDR_DEBUG_CHECKS: %s", msg);
   return GDR_OK;
 }
@@ -784,7 +778,6 @@ gdr_status gdr_attn_decode(const gdr_attn_desc* d, const void* q, const void* k,
   if (!workspace || workspace_bytes < need)
     return fail(GDR_ERR_INVALID_ARG, "workspace of %zu bytes required (got %zu)", need, workspace ? workspace_bytes : 0);
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return fail(GDR_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if ((st = debug_check_cache_lens(cache_lens, d->num_seqs, d->cache_len, stream)) != GDR_OK) return st;
   if ((st = debug_poison(workspace, need, stream)) != GDR_OK) return st;
   a.q = q;
   a.k = k;

@@ -1,5 +1,5 @@
 // Host-side checks of the index arrays the kernels trust: packed sequence
-// offsets, state-pool indices and KV-cache lengths.  The C ABI runs them on a
+// offsets and state-pool indices.  The C ABI runs them on a
 // host copy of the device array when GDR_DEBUG_CHECKS is set (include/gdr.h);
 // they are plain C++ so that the sanitizer build tests them without a GPU.
 #pragma once
@@ -47,18 +47,6 @@ inline bool check_state_indices(const int32_t* idx, int N, int pool, char* msg, 
       return false;
     }
     seen[(size_t)s] = 1;
-  }
-  return true;
-}
-
-// Cached tokens of each decode row: 0 <= len < cache_len (the new token's
-// own slot must fit in the cache).
-inline bool check_cache_lens(const int32_t* lens, int N, int cache_len, char* msg, size_t n) {
-  for (int i = 0; i < N; ++i) {
-    if (lens[i] < 0 || lens[i] >= cache_len) {
-      snprintf(msg, n, "cache_lens[%d] = %d, must lie in [0, %d)", i, lens[i], cache_len);
-      return false;
-    }
   }
   return true;
 }

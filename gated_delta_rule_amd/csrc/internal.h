@@ -121,6 +121,10 @@ hipError_t launch_chunk_f32(const ChunkArgs& a, hipStream_t st);
 // runs in two stages: kStagePrepare fills the workspace (state-independent
 // per-chunk factors), kStageRecur carries the state through the chunks.
 constexpr int kStagePrepare = 1, kStageRecur = 2;
+// Value heads per key head the bf16-MFMA prefill takes: its prepare kernel
+// keeps 512 bytes of LDS per value head of a key head (four workgroups per
+// compute unit up to 8).
+constexpr int kChunkMaxHeadRatio = 64;
 size_t chunk_bf16_workspace_bytes(const ChunkArgs& a);
 hipError_t launch_chunk_bf16(const ChunkArgs& a, void* workspace, hipStream_t st, int stages);
 hipError_t launch_conv_front(const ConvArgs& a, hipStream_t st);

@@ -150,7 +150,8 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
     s_sin[tid] = sinf(r);
   }
   __syncthreads();
-  const bool to_cache = a.k_cache && pos < a.cache_len;
+  // a decode row whose position lies outside the cache is a padding row: no cache write
+  const bool to_cache = a.k_cache && pos >= 0 && pos < a.cache_len;
   for (int hh = wave; hh < a.Hq + a.Hk; hh += 4) {
     const bool is_q = hh < a.Hq;
     const int h = is_q ? hh : hh - a.Hq;
@@ -517,7 +518,10 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecArgs a) {
   const int kvh = nk % a.Hk, n = nk / a.Hk;
   if (n >= a.N) return;
   const int G = a.Hq / a.Hk;
-  const int len = a.cache_lens[n] + 1;
+  // a row whose position lies outside [0, cache_len) is a padding row: every
+  // split reports an empty part (and attn_combine_kernel writes zeros)
+  const int pos = a.cache_lens[n];
+  const int len = (pos >= 0 && pos < a.cache_len) ? pos + 1 : 0;
   const int kb = split * a.split_keys;
   const int col = lane & 15, grp = lane >> 4;
   float* part = a.part + ((((size_t)n * a.Hk + kvh) * a.nsplit + split) * G) * (kAD + 2);
@@ -623,10 +627,16 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(DecArgs a) {
 // out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s * sigmoid(gate).
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part, const uint16_t* gate,
                                                            const int32_t* cache_lens, uint16_t* out, int Hq, int Hk,
-                                                           int nsplit, int split_keys) {
+                                                           int nsplit, int split_keys, int cache_len) {
   const int n = blockIdx.x / Hq, h = blockIdx.x % Hq, d = threadIdx.x;
   const int G = Hq / Hk, kvh = h / G, c = h % G;
-  const int used = (cache_lens[n] + 1 + split_keys - 1) / split_keys;
+  const size_t at = ((size_t)n * Hq + h) * kAD + d;
+  const int pos = cache_lens[n];
+  if (pos < 0 || pos >= cache_len) {  // padding row
+    out[at] = 0;
+    return;
+  }
+  const int used = (pos + 1 + split_keys - 1) / split_keys;
   const float* p = part + (((size_t)n * Hk + kvh) * nsplit * G + c) * (kAD + 2);
   const size_t stride = (size_t)G * (kAD + 2);
   float M = -INFINITY;
@@ -637,7 +647,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* part, co
     num += w * p[s * stride + d];
     den += w * p[s * stride + kAD + 1];
   }
-  const size_t at = ((size_t)n * Hq + h) * kAD + d;
   const float z = bf16_to_f32(gate[at]);
   out[at] = f32_to_bf16(num / den * (1.f / (1.f + __expf(-z))));
 }
@@ -693,7 +702,7 @@ hipError_t launch_attn_decode(const AttnArgs& a, void* ws, hipStream_t st) {
   hipLaunchKernelGGL(attn_decode_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, d);
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.N * a.Hq)), dim3(256), 0, st, part,
                      static_cast<const uint16_t*>(a.gate), a.cache_lens, static_cast<uint16_t*>(a.out), a.Hq, a.Hk,
-                     nsplit, sk);
+                     nsplit, sk, a.cache_len);
   return hipGetLastError();
 }
 

@@ -256,6 +256,8 @@ struct __align__(16) PrepSmem {
   float rk[kC], pr[kC];
 };  // followed in LDS by the per-head log2 decays and beta r_k, [G][64] each
 static_assert(sizeof(PrepSmem) <= 40 * 1024, "four prepare workgroups per compute unit");
+static_assert(sizeof(PrepSmem) + 2 * kChunkMaxHeadRatio * kC * sizeof(float) <= 160 * 1024,
+              "the largest value-head ratio must fit the LDS of one compute unit");
 
 __global__ __launch_bounds__(kNT, 4) void chunk_prep_kernel(ChunkArgs a, unsigned char* ws) {
   extern __shared__ __align__(16) unsigned char smem_raw[];

@@ -1,9 +1,13 @@
 // Roofline probes (include/gdr_roofline.h): achievable HBM streaming rates
-// and the bf16 matrix-core issue rate of the GPU they run on.
+// and the bf16 matrix-core issue rate of the GPU they run on, and two
+// exhaustive checks of the numeric behaviour the conv front's bit-exact
+// contract relies on.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
 #include "gdr_roofline.h"
+#include "silu32.h"
 
 namespace {
 
@@ -77,6 +81,64 @@ __global__ __launch_bounds__(256) void mfma_kernel(float* out, int iters) {
   if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = r;
 }
 
+// Sum of the wave's mismatch counts and minimum of its first mismatching
+// patterns, added to the totals by lane 0 (vector atomics).
+__device__ __forceinline__ void report(unsigned long long nbad, uint32_t first, unsigned long long* bad,
+                                       uint32_t* first_bad) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    nbad += __shfl_xor(nbad, m, 64);
+    first = min(first, (uint32_t)__shfl_xor((int)first, m, 64));
+  }
+  if ((threadIdx.x & 63) == 0 && nbad) {
+    atomicAdd(bad, nbad);
+    atomicMin(first_bad, first);
+  }
+}
+
+// silu32_mid against silu32 for the fp32 patterns lo .. lo + count - 1 whose
+// value lies in [-80, 80] (others, NaN included, are skipped).
+__global__ __launch_bounds__(256) void silu_mid_probe(uint32_t lo, unsigned long long count,
+                                                      unsigned long long* bad, uint32_t* first_bad) {
+  unsigned long long nbad = 0;
+  uint32_t first = 0xffffffffu;
+  const unsigned long long stride = (unsigned long long)gridDim.x * blockDim.x;
+  for (unsigned long long i = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+    const uint32_t bits = lo + (uint32_t)i;
+    const float v = __uint_as_float(bits);
+    if (!(fabsf(v) <= 80.f)) continue;
+    if (__float_as_uint(gdr::silu32_mid(v)) != __float_as_uint(gdr::silu32(v))) {
+      ++nbad;
+      first = min(first, bits);
+    }
+  }
+  report(nbad, first, bad, first_bad);
+}
+
+// The hardware fp32 -> bf16 conversion against round to nearest even on the
+// bit pattern (u + 0x7fff + bit 16 of u) >> 16; a NaN must give a quiet NaN
+// of the same sign.
+__global__ __launch_bounds__(256) void bf16_rne_probe(uint32_t lo, unsigned long long count,
+                                                      unsigned long long* bad, uint32_t* first_bad) {
+  unsigned long long nbad = 0;
+  uint32_t first = 0xffffffffu;
+  const unsigned long long stride = (unsigned long long)gridDim.x * blockDim.x;
+  for (unsigned long long i = (unsigned long long)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+    const uint32_t bits = lo + (uint32_t)i;
+    const uint32_t hw = gdr::f32_to_bf16(__uint_as_float(bits));
+    bool ok;
+    if ((bits & 0x7fffffffu) > 0x7f800000u)
+      ok = (hw & 0x7fc0u) == 0x7fc0u && (hw >> 15) == (bits >> 31);
+    else
+      ok = hw == ((bits + 0x7fffu + ((bits >> 16) & 1u)) >> 16);
+    if (!ok) {
+      ++nbad;
+      first = min(first, bits);
+    }
+  }
+  report(nbad, first, bad, first_bad);
+}
+
 int launched() { return hipGetLastError() == hipSuccess ? 0 : -3; }
 
 }  // namespace
@@ -101,5 +163,21 @@ extern "C" int gdr_roofline_mfma(float* out, int workgroups, int iters, void* st
   if (!out || workgroups <= 0 || iters <= 0) return -1;
   hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)workgroups), dim3(256), 0, static_cast<hipStream_t>(stream), out,
                      iters);
+  return launched();
+}
+
+extern "C" int gdr_probe_silu_mid(uint32_t first_bits, unsigned long long count, unsigned long long* mismatches,
+                                  uint32_t* first_mismatch, void* stream) {
+  if (!mismatches || !first_mismatch || count == 0 || count > (1ull << 32)) return -1;
+  hipLaunchKernelGGL(silu_mid_probe, dim3(8192), dim3(256), 0, static_cast<hipStream_t>(stream), first_bits, count,
+                     mismatches, first_mismatch);
+  return launched();
+}
+
+extern "C" int gdr_probe_bf16_rne(uint32_t first_bits, unsigned long long count, unsigned long long* mismatches,
+                                  uint32_t* first_mismatch, void* stream) {
+  if (!mismatches || !first_mismatch || count == 0 || count > (1ull << 32)) return -1;
+  hipLaunchKernelGGL(bf16_rne_probe, dim3(8192), dim3(256), 0, static_cast<hipStream_t>(stream), first_bits, count,
+                     mismatches, first_mismatch);
   return launched();
 }

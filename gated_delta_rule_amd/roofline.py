@@ -8,7 +8,8 @@ from typing import Optional
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr_roofline.so")
-EXPORTED = ("gdr_roofline_rmw", "gdr_roofline_read", "gdr_roofline_mfma")
+EXPORTED = ("gdr_roofline_rmw", "gdr_roofline_read", "gdr_roofline_mfma", "gdr_probe_silu_mid",
+            "gdr_probe_bf16_rne")
 SLAB = 65536  # bytes per workgroup of the streaming probes
 MFMA_FLOP_PER_WAVE_ITER = 8 * 16 * 16 * 32 * 2
 
@@ -26,6 +27,8 @@ def load() -> ctypes.CDLL:
         lib.gdr_roofline_rmw.argtypes = [P, Z, ctypes.c_float, ctypes.c_int, P]
         lib.gdr_roofline_read.argtypes = [P, Z, P, P]
         lib.gdr_roofline_mfma.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
+        for name in ("gdr_probe_silu_mid", "gdr_probe_bf16_rne"):
+            getattr(lib, name).argtypes = [ctypes.c_uint32, ctypes.c_ulonglong, P, P, P]
         for name in EXPORTED:
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
@@ -56,3 +59,16 @@ def read(buf: torch.Tensor, sums: torch.Tensor) -> None:
 def mfma(out: torch.Tensor, workgroups: int, iters: int) -> None:
     """workgroups x 4 waves, each iters x 8 bf16 16x16x32 matrix-core ops."""
     _check("gdr_roofline_mfma", load().gdr_roofline_mfma(out.data_ptr(), workgroups, iters, _stream(out)))
+
+
+def contract_probe(name: str, first_bits: int, count: int, device) -> tuple:
+    """Run gdr_probe_<name> over count fp32 patterns from first_bits; returns
+    (mismatches, smallest failing pattern or None)."""
+    bad = torch.zeros(1, device=device, dtype=torch.int64)
+    first = torch.full((1,), -1, device=device, dtype=torch.int32)  # 0xffffffff
+    fn = getattr(load(), f"gdr_probe_{name}")
+    _check(f"gdr_probe_{name}", fn(first_bits, count, bad.data_ptr(), first.data_ptr(), _stream(bad)))
+    torch.cuda.synchronize(device)
+    n = int(bad.item())
+    f = int(first.item()) & 0xFFFFFFFF
+    return n, (None if n == 0 else f)

@@ -31,9 +31,9 @@
  *   - Debug mode: with the environment variable GDR_DEBUG_CHECKS set (and not
  *     "0"), read at every call, each entry point first copies the index
  *     arrays it would trust to the host and checks them -- cu_seqlens
- *     (cu[0] == 0, non-decreasing, cu[N] == the token count), state_indices
- *     (no pool slot named twice), cache_lens (0 <= len < cache_len) -- and
- *     returns GDR_ERR_INVALID_ARG naming the first bad entry; then it fills
+ *     (cu[0] == 0, non-decreasing, cu[N] == the token count) and
+ *     state_indices (no pool slot named twice) -- and returns
+ *     GDR_ERR_INVALID_ARG naming the first bad entry; then it fills
  *     its workspace with 0xFF bytes (NaN in fp32 and bf16) before the
  *     kernels run, so that a read of a workspace entry no kernel wrote shows
  *     up as NaN in the results.  The copies wait for `stream` to drain; a
@@ -501,8 +501,9 @@ gdr_status gdr_attn_decode_workspace_size(const gdr_attn_desc* d, size_t* bytes)
  *                cache_lens[n]
  *   cache_lens   [N] int32 device array: tokens already cached; the token sits
  *                at that position and attends to positions 0 .. cache_lens[n].
- *                Must be < cache_len (trusted).  Not modified: the caller
- *                advances it.
+ *                A value outside [0, cache_len) marks a padding row: its out
+ *                is zero and neither cache is written.  Not modified: the
+ *                caller advances it.
  *   out          [N, Hq, 256] bf16
  *   workspace    >= gdr_attn_decode_workspace_size bytes, 256-byte aligned
  * The keys are split into pieces of 256 to 2048 positions (chosen from N, Hk

@@ -15,6 +15,7 @@
 #define GDR_ROOFLINE_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -44,6 +45,28 @@ int gdr_roofline_read(const float* buf, size_t bytes, float* sums, void* stream)
  * FLOPs: workgroups * 4 * iters * 8 * 16384.  workgroups, iters > 0.
  */
 int gdr_roofline_mfma(float* out, int workgroups, int iters, void* stream);
+
+/*
+ * Exhaustive checks of the numeric behaviour that the conv front's bit-exact
+ * contract (SiLU by exp32 and an IEEE division, then round to nearest even to
+ * bf16; deepmagic page, architecture section: the kernel-4 causal conv and
+ * SiLU in front of the recurrence) relies on, run over the fp32 bit patterns
+ * first_bits .. first_bits + count - 1 (count <= 2^32, wrapping past
+ * 0xffffffff).  *mismatches (zeroed by the caller) gains the number of
+ * patterns that fail; *first_mismatch (set to 0xffffffff by the caller) is
+ * lowered to the smallest failing pattern.
+ *   silu_mid: the conv kernel's SiLU for |v| <= 80 (one residual correction
+ *             of v * rcp(d)) equals the contract's SiLU (v / d with the IEEE
+ *             division) bit for bit; patterns outside [-80, 80] and NaN are
+ *             skipped
+ *   bf16_rne: the hardware fp32 -> bf16 conversion equals round to nearest
+ *             even on the bit pattern, and turns a NaN into a quiet NaN of
+ *             the same sign
+ */
+int gdr_probe_silu_mid(uint32_t first_bits, unsigned long long count, unsigned long long* mismatches,
+                       uint32_t* first_mismatch, void* stream);
+int gdr_probe_bf16_rne(uint32_t first_bits, unsigned long long count, unsigned long long* mismatches,
+                       uint32_t* first_mismatch, void* stream);
 
 #ifdef __cplusplus
 }

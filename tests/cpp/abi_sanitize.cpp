@@ -53,12 +53,6 @@ static void index_checks() {
   const int32_t idx_dup[] = {2, 0, 2};
   EXPECT(!gdr::check_state_indices(idx_dup, 3, 4, msg, sizeof msg) && strstr(msg, "twice"));
   EXPECT(gdr::check_state_indices(idx_dup, 3, 0, msg, sizeof msg));  // empty pool: all padding
-  const int32_t lens_ok[] = {0, 63};
-  EXPECT(gdr::check_cache_lens(lens_ok, 2, 64, msg, sizeof msg));
-  const int32_t lens_bad[] = {0, 64};
-  EXPECT(!gdr::check_cache_lens(lens_bad, 2, 64, msg, sizeof msg) && strstr(msg, "cache_lens[1]"));
-  const int32_t lens_neg[] = {-1};
-  EXPECT(!gdr::check_cache_lens(lens_neg, 1, 64, msg, sizeof msg));
 }
 
 static void abi_checks() {

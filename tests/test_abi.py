@@ -75,6 +75,7 @@ def _chunk(d, q=FAKE, cu=None, o=FAKE, init=None, fin=None, entry="gdr_chunk_fwd
     (dict(num_k_heads=0), -1, "positive"),
     (dict(l2norm_eps=-1.0), -1, "eps"),
     (dict(struct_size=8), -1, "struct_size"),
+    (dict(num_k_heads=1, num_v_heads=65), -2, "value heads per key head"),
 ])
 @pytest.mark.parametrize("entry", CHUNK_ENTRIES)
 def test_chunk_fwd_rejects_bad_descriptors(kw, status, msg, entry):

@@ -289,3 +289,37 @@ def test_decode_full_cache():
     qrot = np.stack([to_host(_gpu_qrot_at(q[n], k[n], qw, kw, p, dev)[0]) for n, p in enumerate(lens)])
     r = aref.core_decode(qrot, x.gate, to_host(kc), v_cache_natural(to_host(vc)), np.asarray(lens) + 1)
     _check_out(to_host(out), r["out"], r["mass"])
+
+
+def test_decode_padding_rows():
+    """A decode row whose cache_lens entry lies outside [0, cache_len) is a
+    padding row: zero output, neither cache written, and the other rows equal
+    the same call without the padding rows, bit for bit."""
+    import gated_delta_rule_amd as gdr
+    import torch
+    dev = gpu()
+    L, lens = 128, [5, -1, 127, 128, 70, 1 << 20]
+    live = [i for i, p in enumerate(lens) if 0 <= p < L]
+    N = len(lens)
+    x = synth.attn_inputs(52, lengths=(1,) * N)
+    rng = synth.rng(53)
+    kc0 = synth.round_bf16(rng.standard_normal((N, L, 4, 256)))
+    vc0 = synth.round_bf16(rng.standard_normal((N, L, 4, 256)))
+    say(f"attention decode padding rows lens {lens}")
+    q, k, v, g, qw, kw, _ = _dev(x, dev)
+    kc, vc = to_dev(kc0, "bf16", dev), to_dev(v_cache_blocked(vc0), "bf16", dev)
+    out = gdr.attn_decode(q, k, v, g, qw, kw, kc, vc, torch.tensor(lens, device=dev, dtype=torch.int32))
+    # the same live rows alone
+    sel = torch.tensor(live, device=dev)
+    kc2, vc2 = to_dev(kc0[live], "bf16", dev), to_dev(v_cache_blocked(vc0[live]), "bf16", dev)
+    out2 = gdr.attn_decode(q[sel].contiguous(), k[sel].contiguous(), v[sel].contiguous(), g[sel].contiguous(), qw,
+                           kw, kc2, vc2, torch.tensor([lens[i] for i in live], device=dev, dtype=torch.int32))
+    torch.cuda.synchronize()
+    assert bits_equal(out[sel].contiguous(), out2)
+    assert bits_equal(kc[sel].contiguous(), kc2) and bits_equal(vc[sel].contiguous(), vc2)
+    for i in range(N):
+        if i in live:
+            continue
+        assert not torch.any(out[i].float() != 0), f"padding row {i} has output"
+        assert np.array_equal(to_host(kc[i]), kc0[i]), f"padding row {i} wrote the k cache"
+        assert np.array_equal(v_cache_natural(to_host(vc[i:i + 1]))[0], vc0[i]), f"padding row {i} wrote the v cache"

@@ -100,7 +100,7 @@ def test_decode_debug_mode_rejects_a_slot_named_twice():
         _expect_invalid(lambda: gdr_amd.recurrent_step(q, k, v, g, beta, pool.clone(), state_indices=dup), "twice")
 
 
-def test_conv_and_attention_debug_mode():
+def test_conv_debug_mode():
     import torch
     import gated_delta_rule_amd as gdr_amd
     dev = gpu()
@@ -117,17 +117,3 @@ def test_conv_and_attention_debug_mode():
         bad = to_dev(np.asarray([0, 80, 70], np.int32), "i32", dev)
         _expect_invalid(lambda: gdr_amd.conv_gate_fused(bf(p.x), bf(p.conv_w), bad, f32(p.a), f32(p.b),
                                                         f32(p.A_log), f32(p.dt_bias), p.hk, p.hv, p.d), "decreases")
-    say("debug checks: attention decode cache lengths")
-    a = synth.attn_inputs(83, lengths=(2,))
-    N, L = 2, 64
-    q, gate = bf(a.q[:N]), bf(a.gate[:N])
-    k, v = bf(a.k[:N]), bf(a.v[:N])
-    kc = torch.zeros((N, L, k.shape[1], 256), device=dev, dtype=torch.bfloat16)
-    vc = torch.zeros((N, k.shape[1], L // 32, 256, 32), device=dev, dtype=torch.bfloat16)
-    with debug_checks():
-        lens = to_dev(np.asarray([3, 63], np.int32), "i32", dev)
-        gdr_amd.attn_decode(q, k, v, gate, f32(a.q_norm_w), f32(a.k_norm_w), kc, vc, lens)
-        torch.cuda.synchronize()
-        bad = to_dev(np.asarray([3, 64], np.int32), "i32", dev)
-        _expect_invalid(lambda: gdr_amd.attn_decode(q, k, v, gate, f32(a.q_norm_w), f32(a.k_norm_w), kc, vc, bad),
-                        "cache_lens[1]")

@@ -61,3 +61,36 @@ def test_probes_compute_what_they_say():
     roofline.mfma(out, 8, 3)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
+
+
+def test_contract_probes_reject_bad_arguments():
+    lib = roofline.load()
+    fake = ctypes.c_void_p(1 << 20)
+    for name in ("gdr_probe_silu_mid", "gdr_probe_bf16_rne"):
+        fn = getattr(lib, name)
+        assert fn(0, 0, fake, fake, None) == -1
+        assert fn(0, (1 << 32) + 1, fake, fake, None) == -1
+        assert fn(0, 16, None, fake, None) == -1
+
+
+@pytest.mark.gpu
+def test_conv_silu_shortcut_equals_ieee_division_on_all_of_minus80_to_80():
+    """The conv kernel's SiLU for |v| <= 80 (rcp plus one residual
+    correction) gives the contract's IEEE-division SiLU bit for bit on every
+    fp32 value in [-80, 80] (about 2.2e9 patterns)."""
+    dev = gpu()
+    say("contract probe: silu32_mid vs silu32 on [-80, 80]")
+    top = 0x42A00000  # 80.0
+    for lo in (0x00000000, 0x80000000):
+        n, first = roofline.contract_probe("silu_mid", lo, top + 1, dev)
+        assert n == 0, f"{n} mismatches, first at pattern {first:#010x}"
+
+
+@pytest.mark.gpu
+def test_hardware_bf16_conversion_is_round_to_nearest_even():
+    """The fp32 -> bf16 conversion the kernels use rounds to nearest even on
+    every one of the 2^32 fp32 patterns (NaN to a quiet NaN of its sign)."""
+    dev = gpu()
+    say("contract probe: fp32 -> bf16 on all 2^32 patterns")
+    n, first = roofline.contract_probe("bf16_rne", 0, 1 << 32, dev)
+    assert n == 0, f"{n} mismatches, first at pattern {first:#010x}"
