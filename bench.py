@@ -176,9 +176,13 @@ def bench_roofline(reps: int = 10):
     out = torch.empty(wgs * 4, device=dev)
     flop = wgs * 4 * iters * roofline.MFMA_FLOP_PER_WAVE_ITER
     mfma = flop / (timed(lambda: roofline.mfma(out, wgs, iters)) * 1e-3) / 1e12
-    log(f"roofline probes: rmw nt {rmw_nt:.0f} GB/s, rmw {rmw:.0f} GB/s, read {rd:.0f} GB/s, mfma {mfma:.0f} TFLOP/s")
+    valu_iters = 20000
+    valu = (wgs * 4 * valu_iters * roofline.VALU_INSTS_PER_WAVE_ITER
+            / (timed(lambda: roofline.valu(out, wgs, valu_iters)) * 1e-3) / cus)
+    log(f"roofline probes: rmw nt {rmw_nt:.0f} GB/s, rmw {rmw:.0f} GB/s, read {rd:.0f} GB/s, mfma {mfma:.0f} TFLOP/s, "
+        f"valu {valu / 1e9:.3f} G wave-instructions/s per CU")
     return {"hbm_rmw_nontemporal_GBps": rmw_nt, "hbm_rmw_GBps": rmw, "hbm_read_GBps": rd,
-            "mfma_bf16_TFLOPs": mfma, "buffer_bytes": nbytes}
+            "mfma_bf16_TFLOPs": mfma, "valu_wave_insts_per_s_per_cu": valu, "buffer_bytes": nbytes}
 
 
 def gpu_clocks():
@@ -199,10 +203,13 @@ def gpu_clocks():
     return out or None
 
 
-def bench_decode(steps: int = 256, replicas: int = 1, pool: int = 0):
+def bench_decode(steps: int = 256, replicas: int = 1, pool: int = 0, shuffled: bool = True):
     """Decode steps of 64 sequences.  replicas > 1 cycles through that many
     copies of the state set; pool > 0 keeps the states in a pool of that many
-    slots (gdr_recurrent_step_indexed) with the rows naming shuffled slots."""
+    slots (gdr_recurrent_step_indexed) with the rows naming shuffled slots
+    (shuffled=True) or slots 0..63 in row order.  frac_hbm counts every
+    algorithmic byte (state read and written, q, k, v, gates, o);
+    frac_hbm_state_only the state alone."""
     import torch
     import gated_delta_rule_amd as gdr
     from inputs import synth
@@ -211,7 +218,7 @@ def bench_decode(steps: int = 256, replicas: int = 1, pool: int = 0):
     log(f"decode: N={N}, {steps} steps, " + (f"pool of {pool} slots" if pool else f"{replicas} state replica(s)"))
     A_log, dt, s0 = synth.decode_inputs(N=N)
     if pool:
-        perm = np.random.default_rng(7).permutation(pool)[:N]
+        perm = np.random.default_rng(7).permutation(pool)[:N] if shuffled else np.arange(N)
         slots = torch.zeros((pool, HV, D, D), device=dev)
         slots[torch.as_tensor(perm, device=dev)] = torch.from_numpy(s0).to(dev)
         idx = torch.as_tensor(perm.astype(np.int32), device=dev)
@@ -242,7 +249,9 @@ def bench_decode(steps: int = 256, replicas: int = 1, pool: int = 0):
     other = N * (2 * HK * D * 2 + HV * D * 2 + 2 * HV * 4 + HV * D * 4)
     return dict(us_per_step=ms * 1e3, state_GBps=state_bytes / (ms * 1e-3) / 1e9,
                 total_GBps=(state_bytes + other) / (ms * 1e-3) / 1e9,
-                frac_hbm=state_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, working_set_MiB=replicas * state_bytes / 2 / 2**20)
+                frac_hbm=(state_bytes + other) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                frac_hbm_state_only=state_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                working_set_MiB=replicas * state_bytes / 2 / 2**20)
 
 
 def bench_decode_layer(steps: int = 128):
@@ -250,7 +259,8 @@ def bench_decode_layer(steps: int = 128):
     gdr_decode_layer_step against the same work as three launches
     (gdr_conv_gate_fused on one-token sequences, gdr_recurrent_step,
     gdr_gated_rmsnorm).  Bytes counted: the recurrent state read and written,
-    plus x, the conv state (read and written), a, b, z and y."""
+    plus x, the conv state (read and written), a, b, z and y; frac_hbm counts
+    them all, frac_hbm_state_only the recurrent state alone."""
     import torch
     import gated_delta_rule_amd as gdr
     from inputs import synth
@@ -304,7 +314,8 @@ def bench_decode_layer(steps: int = 128):
     other = N * (C * 2 + 2 * C * 3 * 2 + 2 * HV * 4 + 2 * HV * D * 2)
     return dict(us_per_step=ms_f * 1e3, state_GBps=state_bytes / (ms_f * 1e-3) / 1e9,
                 total_GBps=(state_bytes + other) / (ms_f * 1e-3) / 1e9,
-                frac_hbm=state_bytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                frac_hbm=(state_bytes + other) / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                frac_hbm_state_only=state_bytes / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 three_launches_us_per_step=ms_u * 1e3)
 
 
@@ -678,6 +689,7 @@ def main():
         if args.only == "all":
             out["decode_2_replicas"] = bench_decode(replicas=2)
             out["decode_pool_indexed"] = bench_decode(pool=128)
+            out["decode_pool_in_order"] = bench_decode(pool=128, shuffled=False)
             out["decode_layer"] = bench_decode_layer()
     if args.only == "decode_layer":
         out["decode_layer"] = bench_decode_layer()
@@ -694,7 +706,7 @@ def main():
             out["roofline"]["frac_of_achievable"] = out["roofline"]["achieved"] / ach["mfma_bf16_TFLOPs"]
             out["roofline"]["hbm"]["frac_of_achievable"] = (out["roofline"]["hbm"]["achieved"]
                                                             / ach["hbm_rmw_nontemporal_GBps"])
-        for key in ("decode", "decode_2_replicas", "decode_pool_indexed", "decode_layer"):
+        for key in ("decode", "decode_2_replicas", "decode_pool_indexed", "decode_pool_in_order", "decode_layer"):
             if key in out:
                 out[key]["frac_of_achievable"] = out[key]["state_GBps"] / ach["hbm_rmw_nontemporal_GBps"]
     out["clocks"] = {"before": clocks_before, "after": gpu_clocks()}

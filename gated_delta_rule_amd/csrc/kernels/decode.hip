@@ -85,14 +85,17 @@ __global__ __launch_bounds__(256) void decode_kernel(const TQ* __restrict__ q, c
       kv[j][e] = load_as_f32(kp + 32 * j + e);
       qv[j][e] = load_as_f32(qp + 32 * j + e);
     }
+  // Every multiply-add below is an explicit fma, so that the fused
+  // decode-layer kernel, which spells out the same operations, gives the same
+  // bits whatever the compiler would contract on its own.
   float kk = 0.f, qq = 0.f, kq = 0.f;
 #pragma unroll
   for (int j = 0; j < F4; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      kk += kv[j][e] * kv[j][e];
-      qq += qv[j][e] * qv[j][e];
-      kq += kv[j][e] * qv[j][e];
+      kk = __builtin_fmaf(kv[j][e], kv[j][e], kk);
+      qq = __builtin_fmaf(qv[j][e], qv[j][e], qq);
+      kq = __builtin_fmaf(kv[j][e], qv[j][e], kq);
     }
   kk = sum8(kk);
   qq = sum8(qq);
@@ -124,18 +127,18 @@ __global__ __launch_bounds__(256) void decode_kernel(const TQ* __restrict__ q, c
     for (int j = 0; j < F4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pu += s[i][j][e] * kv[j][e];
-        pw += s[i][j][e] * qv[j][e];
+        pu = __builtin_fmaf(s[i][j][e], kv[j][e], pu);
+        pw = __builtin_fmaf(s[i][j][e], qv[j][e], pw);
       }
     pu = sum8(pu);
     pw = sum8(pw);
-    const float delta = b * (load_as_f32(vp + r) - alpha * pu);
-    if (e8 == 0) store_from_f32(op + r, scale * (alpha * pw + delta * kq));
+    const float delta = b * __builtin_fmaf(-alpha, pu, load_as_f32(vp + r));
+    if (e8 == 0) store_from_f32(op + r, scale * __builtin_fmaf(delta, kq, alpha * pw));
 #pragma unroll
     for (int j = 0; j < F4; ++j) {
       f32x4 ns;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ns[e] = alpha * s[i][j][e] + delta * kv[j][e];
+      for (int e = 0; e < 4; ++e) ns[e] = __builtin_fmaf(delta, kv[j][e], alpha * s[i][j][e]);
       __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + (size_t)r * D + 32 * j + 4 * e8));
     }
   }

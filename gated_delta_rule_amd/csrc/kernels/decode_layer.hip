@@ -18,8 +18,9 @@
 //   phase 1  conv + SiLU of the (2 + G) * 128 channels under the front's
 //            bit-exact contract (same code as the prefill front), the
 //            conv state rolled by one token, the gates; results to LDS
-//   phase 2  the state update and o, with the decode kernel's arithmetic and
-//            reduction order (so o and S match gdr_recurrent_step bit for bit),
+//   phase 2  the state update and o, with the decode kernel's arithmetic,
+//            fma for fma, and reduction order (so o and S match
+//            gdr_recurrent_step bit for bit),
 //            in two passes of two row steps: as the first pass writes a row
 //            back, the registers it held load the matching second-pass row,
 //            so those loads stream under the first pass's arithmetic and
@@ -149,9 +150,9 @@ __global__ __launch_bounds__(256 * G) void decode_layer_kernel(LayerStepArgs a) 
   for (int j = 0; j < F4; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      kk += kv[j][e] * kv[j][e];
-      qq += qv[j][e] * qv[j][e];
-      kq += kv[j][e] * qv[j][e];
+      kk = __builtin_fmaf(kv[j][e], kv[j][e], kk);
+      qq = __builtin_fmaf(qv[j][e], qv[j][e], qq);
+      kq = __builtin_fmaf(kv[j][e], qv[j][e], kq);
     }
   kk = sum8(kk);
   qq = sum8(qq);
@@ -183,14 +184,14 @@ __global__ __launch_bounds__(256 * G) void decode_layer_kernel(LayerStepArgs a) 
     for (int j = 0; j < F4; ++j)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pu += s[i][j][e] * kv[j][e];
-        pw += s[i][j][e] * qv[j][e];
+        pu = __builtin_fmaf(s[i][j][e], kv[j][e], pu);
+        pw = __builtin_fmaf(s[i][j][e], qv[j][e], pw);
       }
     pu = sum8(pu);
     pw = sum8(pw);
-    const float delta = b * (xs[2 * D + gh * D + r] - alpha * pu);
+    const float delta = b * __builtin_fmaf(-alpha, pu, xs[2 * D + gh * D + r]);
     if (e8 == 0) {
-      const float ov = a.scale * (alpha * pw + delta * kq);
+      const float ov = a.scale * __builtin_fmaf(delta, kq, alpha * pw);
       os[gh][r] = ov;
       if (a.o) a.o[(size_t)n * HvD + h * D + r] = ov;
     }
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(256 * G) void decode_layer_kernel(LayerStepArgs a) 
     for (int j = 0; j < F4; ++j) {
       f32x4 ns;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ns[e] = alpha * s[i][j][e] + delta * kv[j][e];
+      for (int e = 0; e < 4; ++e) ns[e] = __builtin_fmaf(delta, kv[j][e], alpha * s[i][j][e]);
       __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(S + (size_t)r * D + 32 * j + 4 * e8));
     }
     if (pass == 0) {

@@ -81,6 +81,25 @@ __global__ __launch_bounds__(256) void mfma_kernel(float* out, int iters) {
   if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = r;
 }
 
+// Vector-ALU issue: 8 independent chains of a = a * m + c per thread, the
+// multiply and the add issued as two fp32 instructions (no contraction), so
+// every wave issues 16 VALU instructions per round with no dependency stall.
+__global__ __launch_bounds__(256) void valu_kernel(float* out, int iters) {
+#pragma clang fp contract(off)
+  const float m = 0.999f + 1e-7f * (float)(threadIdx.x & 63), c = 1e-3f * (float)(threadIdx.x & 7);
+  float acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = (float)(u + 1);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = acc[u] * m + c;
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) r += acc[u];
+  if ((threadIdx.x & 63) == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = r;
+}
+
 // Sum of the wave's mismatch counts and minimum of its first mismatching
 // patterns, added to the totals by lane 0 (vector atomics).
 __device__ __forceinline__ void report(unsigned long long nbad, uint32_t first, unsigned long long* bad,
@@ -162,6 +181,13 @@ extern "C" int gdr_roofline_read(const float* buf, size_t bytes, float* sums, vo
 extern "C" int gdr_roofline_mfma(float* out, int workgroups, int iters, void* stream) {
   if (!out || workgroups <= 0 || iters <= 0) return -1;
   hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)workgroups), dim3(256), 0, static_cast<hipStream_t>(stream), out,
+                     iters);
+  return launched();
+}
+
+extern "C" int gdr_roofline_valu(float* out, int workgroups, int iters, void* stream) {
+  if (!out || workgroups <= 0 || iters <= 0) return -1;
+  hipLaunchKernelGGL(valu_kernel, dim3((unsigned)workgroups), dim3(256), 0, static_cast<hipStream_t>(stream), out,
                      iters);
   return launched();
 }

@@ -8,10 +8,11 @@ from typing import Optional
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdr_roofline.so")
-EXPORTED = ("gdr_roofline_rmw", "gdr_roofline_read", "gdr_roofline_mfma", "gdr_probe_silu_mid",
-            "gdr_probe_bf16_rne")
+EXPORTED = ("gdr_roofline_rmw", "gdr_roofline_read", "gdr_roofline_mfma", "gdr_roofline_valu",
+            "gdr_probe_silu_mid", "gdr_probe_bf16_rne")
 SLAB = 65536  # bytes per workgroup of the streaming probes
 MFMA_FLOP_PER_WAVE_ITER = 8 * 16 * 16 * 32 * 2
+VALU_INSTS_PER_WAVE_ITER = 16
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -27,6 +28,7 @@ def load() -> ctypes.CDLL:
         lib.gdr_roofline_rmw.argtypes = [P, Z, ctypes.c_float, ctypes.c_int, P]
         lib.gdr_roofline_read.argtypes = [P, Z, P, P]
         lib.gdr_roofline_mfma.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
+        lib.gdr_roofline_valu.argtypes = [P, ctypes.c_int, ctypes.c_int, P]
         for name in ("gdr_probe_silu_mid", "gdr_probe_bf16_rne"):
             getattr(lib, name).argtypes = [ctypes.c_uint32, ctypes.c_ulonglong, P, P, P]
         for name in EXPORTED:
@@ -59,6 +61,11 @@ def read(buf: torch.Tensor, sums: torch.Tensor) -> None:
 def mfma(out: torch.Tensor, workgroups: int, iters: int) -> None:
     """workgroups x 4 waves, each iters x 8 bf16 16x16x32 matrix-core ops."""
     _check("gdr_roofline_mfma", load().gdr_roofline_mfma(out.data_ptr(), workgroups, iters, _stream(out)))
+
+
+def valu(out: torch.Tensor, workgroups: int, iters: int) -> None:
+    """workgroups x 4 waves, each iters x 16 independent fp32 VALU instructions."""
+    _check("gdr_roofline_valu", load().gdr_roofline_valu(out.data_ptr(), workgroups, iters, _stream(out)))
 
 
 def contract_probe(name: str, first_bits: int, count: int, device) -> tuple:

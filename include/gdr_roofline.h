@@ -1,6 +1,6 @@
 /*
- * Roofline probes for MI355X (gfx950): the achievable HBM bandwidth and bf16
- * matrix-core rate of the machine they run on, measured beside the path's
+ * Roofline probes for MI355X (gfx950): the achievable HBM bandwidth, bf16
+ * matrix-core rate and vector-ALU issue rate of the machine they run on, measured beside the path's
  * own kernels so that each kernel can be placed against what the hardware
  * delivers as well as against the datasheet peaks (HBM 8 TB/s, dense bf16
  * 2.5 PFLOP/s).  libgdr_roofline.so is a measurement aid and no part of the
@@ -45,6 +45,17 @@ int gdr_roofline_read(const float* buf, size_t bytes, float* sums, void* stream)
  * FLOPs: workgroups * 4 * iters * 8 * 16384.  workgroups, iters > 0.
  */
 int gdr_roofline_mfma(float* out, int workgroups, int iters, void* stream);
+
+/*
+ * Vector-ALU issue: `workgroups` workgroups of 256 threads, each thread
+ * running `iters` rounds of 8 independent a = a * m + c chains with the
+ * multiply and the add as separate fp32 instructions (16 VALU instructions
+ * per wave per round, no dependency stalls); each wave writes one float to
+ * out[global wave index] (workgroups * 4 floats).  Wave-level VALU
+ * instructions: workgroups * 4 * iters * 16 (plus a few dozen per wave).
+ * workgroups, iters > 0.
+ */
+int gdr_roofline_valu(float* out, int workgroups, int iters, void* stream);
 
 /*
  * Exhaustive checks of the numeric behaviour that the conv front's bit-exact

@@ -35,13 +35,15 @@ def test_bad_arguments_rejected_before_launch():
     assert lib.gdr_roofline_read(fake, 1000, fake, None) == -1
     assert lib.gdr_roofline_mfma(fake, 0, 10, None) == -1
     assert lib.gdr_roofline_mfma(None, 4, 10, None) == -1
+    assert lib.gdr_roofline_valu(fake, 4, 0, None) == -1
+    assert lib.gdr_roofline_valu(None, 4, 10, None) == -1
 
 
 @pytest.mark.gpu
 def test_probes_compute_what_they_say():
     import torch
     dev = gpu()
-    say("roofline probes: rmw, read, mfma")
+    say("roofline probes: rmw, read, mfma, valu")
     n = 4 * 65536 // 4
     x = torch.arange(n, device=dev, dtype=torch.float32) % 1000
     ref = x.clone()
@@ -61,6 +63,19 @@ def test_probes_compute_what_they_say():
     roofline.mfma(out, 8, 3)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
+    # the VALU probe's lane 0 runs a <- a * 0.999f (c = 0) on a = 1..8, in
+    # fp32 with the multiply rounded on its own, and writes the chains' sum
+    out = torch.full((8 * 4,), float("nan"), device=dev)
+    roofline.valu(out, 8, 5)
+    torch.cuda.synchronize()
+    m = np.float32(0.999)
+    acc = [np.float32(u + 1) for u in range(8)]
+    for _ in range(5):
+        acc = [np.float32(a * m) + np.float32(0) for a in acc]
+    r = np.float32(0)
+    for a in acc:
+        r = np.float32(r + a)
+    assert np.all(out.cpu().numpy() == r)
 
 
 def test_contract_probes_reject_bad_arguments():
