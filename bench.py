@@ -10,10 +10,14 @@ tokens/s over the K timed steps.  The same JSON line also reports, measured
 in the same run:
 
   decode    -- 64 sequences x 48 heads of 128x128 fp32 state, one token per
-               step, state updated in place, 256 steps: state GB/s
+               step, state updated in place, 256 steps: state GB/s; also
+               with two state sets, and from a 128-slot state pool with the
+               rows naming shuffled slots and slots in row order
   decode_layer -- one token of the whole layer path for the same 64
                sequences in one launch (conv front, gates, recurrent step,
                gated RMS norm), beside the same work as three launches
+               (the decode entries' frac_hbm counts every algorithmic byte,
+               frac_hbm_state_only the recurrent state alone)
   pipeline  -- the whole layer path over a packed batch of 8 sequences
                (65536 tokens): conv+SiLU+gates, recurrence, gated RMSNorm
   layer     -- one whole delta layer on a 32768-token sequence with synthetic
@@ -33,8 +37,9 @@ in the same run:
                v read, o written, state in and out) against 8 TB/s, and the
                HBM bytes the committed rocprofv3 counters measured for it
   achievable -- the roofline probes (libgdr_roofline.so): streaming HBM
-               read-modify-write and read rates and the dense bf16 matrix-core
-               rate this GPU delivers, beside the datasheet peaks
+               read-modify-write and read rates, the dense bf16 matrix-core
+               rate and the fp32 vector-ALU issue rate this GPU delivers,
+               beside the datasheet peaks
   clocks    -- the driver's current clock levels before and after the run
   cpu_baseline -- the fp64 CPU oracle timed on the host cores on a bounded
                sample of the same workload (the first three 32K-token calls;
