@@ -454,7 +454,7 @@ def bench_layer(reps: int = 5):
                         "weights": "synthetic, N(0, 1/fan_in)"})
 
 
-def bench_attention(reps: int = 3, dec_steps: int = 20):
+def bench_attention(reps: int = 5, dec_steps: int = 20):
     """The global attention layer (24 query / 4 kv heads, d 256): causal
     prefill of one 32768-token sequence (q/k norm + rotary, attention, gate),
     as matrix-core work 4 Hq d T^2 / 2 against the bf16 peak, beside torch's
@@ -481,7 +481,7 @@ def bench_attention(reps: int = 3, dec_steps: int = 20):
     ws = torch.empty(nb.value, device=dev, dtype=torch.uint8)
 
     def timed(fn, n):
-        for _ in range(2):
+        for _ in range(4):  # untimed, until the clocks have settled
             fn()
         torch.cuda.synchronize()
         s0, s1 = _events()

@@ -12,10 +12,12 @@
 //                      of dims (j, j + 32), j < 32; q to a bf16 buffer, k to a
 //                      key buffer padded per sequence to whole 64-key chunks
 //                      (and to the caller's KV cache)
-//   attn_vt_kernel     V transposed per 64-key chunk (dims x keys), so both
-//                      products below read 16 contiguous bytes per lane
+//   attn_vt_kernel     V transposed per 64-key chunk (dims x keys)
 //   attn_fwd_kernel    causal attention, one workgroup per (query head,
-//                      128-query block), 64-key blocks through LDS
+//                      128-query block), 32-key blocks through LDS
+// The keys and V^T go to per-head buffers in the order the matrix cores
+// read them (32-key tiles of 16 KiB, each made of 1 KiB fragments), so
+// that both the copies into LDS and the reads out of it are contiguous.
 // Decode: attn_prep_kernel (one row per sequence, at its cache position,
 // appending k and v to the cache), attn_decode_kernel (split over the cached
 // keys) and attn_combine_kernel (merges the splits, applies the gate).
@@ -37,10 +39,19 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-// One 16-byte direct-to-LDS load per lane: lane l's bytes land at LDS byte
+// One 16-byte direct-to-LDS load per lane from the wave-uniform address
+// base + voff (voff a per-lane byte offset): lane l's bytes land at LDS byte
 // address lds_addr + 16 l.  No register receives data; waits are explicit.
-__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(lds_addr) : "memory", "m0");
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+// A pointer every lane of the wave holds, moved to scalar registers.
+__device__ __forceinline__ const void* wave_uniform(const void* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -103,6 +114,22 @@ __global__ __launch_bounds__(256) void attn_table_kernel(const int32_t* cu, int 
 // RMS norm + rotation of one token's heads.  One workgroup per token (prefill)
 // or per sequence (decode, one new token at its cache position).  Waves take
 // heads round-robin; lane l holds dims 4l .. 4l+3.
+// Fragment order of the prefill's key and V^T buffers.  Each head holds
+// kblocks tiles of 32 keys (16 KiB); 1 KiB fragment f of a tile is what
+// lane l of the attention kernel's matrix-core operand holds, at byte 16 l:
+//   keys: f = dims 16 f .. 16 f + 15; lane l = key l % 32, dims 16 f + 8 (l / 32) .. +7
+//   V^T:  f = 2 dt + g; lane l = dim 32 dt + l % 32, slots 16 g + 8 (l / 32) .. +7
+// (slots: the keys of a tile in the order the probabilities leave the score
+// registers, kperm below).  key and slot count from the head's first padded key.
+__host__ __device__ inline size_t kfrag_index(int h, int64_t kblocks, int64_t key, int d) {
+  return (((size_t)h * kblocks + key / 32) * 16 + d / 16) * 512 + (((d >> 3) & 1) * 32 + key % 32) * 8 + (d & 7);
+}
+__host__ __device__ inline size_t vfrag_index(int h, int64_t kblocks, int64_t slot, int d) {
+  const int s = (int)(slot % 32);
+  return ((size_t)h * kblocks + slot / 32) * (32 * 256) +
+         ((2 * (d >> 5) + (s >> 4)) * 64 + ((s >> 3) & 1) * 32 + (d & 31)) * 8 + (s & 7);
+}
+
 struct PrepArgs {
   const uint16_t *q, *k, *v;     // [rows, Hq | Hk, D] bf16
   const float *q_w, *k_w;        // [D]
@@ -110,10 +137,11 @@ struct PrepArgs {
   const int32_t* table;          // prefill: key-chunk offsets [N+1]
   const int32_t* cache_lens;     // decode: [N] position of the new token
   uint16_t* q_rot;               // [rows, Hq, D]
-  uint16_t* k_pad;               // prefill: [64 * chunks, Hk, D] or NULL
+  uint16_t* k_pad;               // prefill: keys in fragment order (kfrag_index) or NULL
   uint16_t* k_rot;               // [rows, Hk, D] or NULL (the rotated k, unpadded)
   uint16_t *k_cache, *v_cache;   // [N, cache_len, Hk, D] and the blocked layout below, or NULL
   int rows, N, Hq, Hk, cache_len;
+  int64_t kblocks;               // prefill: 32-key tiles per head in k_pad
   float eps;
   double base;
 };
@@ -188,7 +216,7 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
     } else {
       if (a.k_pad) {
         const size_t tp = (size_t)kKB * a.table[n] + pos;
-        *reinterpret_cast<u32x2*>(a.k_pad + (tp * a.Hk + h) * kAD + 4 * lane) = out;
+        *reinterpret_cast<u32x2*>(a.k_pad + kfrag_index(h, a.kblocks, (int64_t)tp, 4 * lane)) = out;
       }
       if (a.k_rot) *reinterpret_cast<u32x2*>(a.k_rot + ((size_t)t * a.Hk + h) * kAD + 4 * lane) = out;
       if (to_cache) {
@@ -207,12 +235,11 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// V transposed per 64-key chunk into two 32-key tiles: vt[h][t][d][slot],
-// t = 2 c + slot / 32, each 256 x 32 tile contiguous (16 KiB, so one copy
-// instruction reads 1 KiB of it), keys in slot
-// order kPerm (within each group of 16 keys the middle two quarters swap),
-// the order in which the attention kernel's probabilities come out of its
-// score registers.  Keys past the sequence end are zero.
+// V transposed per 64-key chunk into two 32-key tiles in fragment order
+// (vfrag_index), keys in slot order kperm (within each group of 16 keys the
+// middle two quarters swap), the order in which the attention kernel's
+// probabilities come out of its score registers.  Keys past the sequence
+// end are zero.
 __device__ __forceinline__ int kperm(int i) {
   const int q = (i >> 2) & 3;
   return (i & ~12) | ((q == 1 ? 2 : q == 2 ? 1 : q) << 2);
@@ -243,8 +270,8 @@ __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* v, const i
     u16x8 pk;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pk[e] = row[s + e];
-    // 32-key tile 2c + s / 32, row d
-    uint16_t* dst = vt + (((size_t)h * (tpad / 32) + 2 * c + s / 32) * kAD + d) * 32 + s % 32;
+    // slots s .. s + 7 of row d
+    uint16_t* dst = vt + vfrag_index(h, tpad / 32, (int64_t)kKB * c + s, d);
     *reinterpret_cast<u16x8*>(dst) = pk;
   }
   if (v_cache) {
@@ -272,20 +299,20 @@ __global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* v, const i
 // ---------------------------------------------------------------------------
 // Causal attention.  Workgroup: one query head, 128 queries of one sequence,
 // 4 waves of 32 queries.  Keys go in blocks of 32 through four LDS stages
-// (K tile [32 keys][256], V^T tile [256 dims][32 keys], 16 KiB each), copied
-// by direct-to-LDS loads three blocks ahead of their use.  Per block j, one
-// wave does
+// (a K tile and a V^T tile of 16 KiB each, in fragment order), copied by
+// direct-to-LDS loads, 1 KiB per instruction, three blocks ahead of their
+// use.  A wave's operand reads are 1 KiB contiguous runs at fixed offsets.
+// Per block j, one wave does
 //   S^T(j+1) = K Q^T   16 MFMAs (32x32x16): lane l holds query l % 32 and 16
-//                      of the block's keys (the other 16 are in lane l ^ 32)
-//   softmax(j)         online, base 2, on the scores of the previous
-//                      iteration, so its VALU work runs beside the MFMAs of
-//                      S(j+1); the accumulator is rescaled only when the
-//                      running maximum grows by more than 8
+//                      of the block's keys (the other 16 are in lane l ^ 32),
+//                      beside the exponentials of block j (VALU)
 //   O^T += V^T P^T(j)  8 dim tiles x 2 key steps, P straight from the score
-//                      registers (bf16)
-// with the block's eight copy pieces spread between the MFMAs.  LDS swizzles
-// put the 16 lanes of one 16-byte read on 16 bank groups: K rows (512 B) use
-// chunk c ^ (row & 15), V^T rows (64 B) c ^ ((row >> 2) & 3).
+//                      registers (bf16), beside the mask and maximum of
+//                      block j+1
+// Softmax is online and in base 2: the running maximum is kept in scaled
+// units, each probability is exp2(s * log2(e)/sqrt(d) - max) with the
+// argument one fma, and the accumulator is rescaled only when the maximum
+// grows by more than 8.
 struct FwdArgs {
   const uint16_t *q_rot, *k_pad, *vt, *gate;
   const int32_t *cu, *table;
@@ -299,9 +326,6 @@ constexpr float kRescale = 8.f;
 constexpr int kFB = 32;    // keys per block
 constexpr int kStg = 4;    // LDS stages
 
-__device__ __forceinline__ bf16x8 lds_frag(const uint16_t* s, int row, int pitch_chunks, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(s + row * pitch_chunks * 8 + 8 * chunk);
-}
 __device__ __forceinline__ void wait_vm8() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
 __device__ __forceinline__ void wait_vm16() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
 
@@ -328,8 +352,8 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
   const int my_q = min(qw + (lane & 31), L - 1);       // this lane's query (rows past L repeat the last)
   const int last_q = min(q0 + kQB - 1, L - 1);
   const int nkb = last_q / kFB + 1;
-  const int64_t kp0 = (int64_t)kKB * a.table[n];       // first padded key of the sequence
-  const int64_t vt0 = (int64_t)kvh * (a.tpad / kFB) + kp0 / kFB;  // its first V^T tile
+  // first tile of the sequence in this kv head's key and V^T buffers
+  const int64_t tile0 = (int64_t)kvh * (a.tpad / kFB) + (int64_t)kKB / kFB * a.table[n];
 
   // Q^T fragments (B operand): query my_q, dims 16 ks + 8 (l / 32) .. +7
   bf16x8 qf[16];
@@ -346,39 +370,48 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
     for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
   float mrun = -INFINITY, lsum = 0.f;
 
+  const uint32_t ldsK = (uint32_t)(uintptr_t)(lds_ptr)(&sK[0][0]), ldsV = (uint32_t)(uintptr_t)(lds_ptr)(&sV[0][0]);
   // piece i (0..7) of the copy of key block jb (clamped to the last block,
-  // so every iteration issues eight) into stage jb % 4: pieces 0..3 are K
-  // rows 8 wave + 2 i .. +1, pieces 4..7 V^T rows 64 wave + 16 (i - 4) .. +15
+  // so every iteration issues eight) into stage jb % 4: pieces 0..3 are the
+  // K fragments 4 wave + i, pieces 4..7 the V^T fragments 4 wave + i - 4
   auto copy_piece = [&](int jb, int i) {
     const int st = jb % kStg;
     jb = min(jb, nkb - 1);
-    if (i < 4) {
-      const int rb = 8 * wave + 2 * i, row = rb + (lane >> 5);
-      const int c = (lane & 31) ^ (row & 15);
-      const uint16_t* g = a.k_pad + ((kp0 + (int64_t)kFB * jb + row) * a.Hk + kvh) * kAD + 8 * c;
-      dma16(g, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)(sK[st] + rb * kAD)));
-    } else {
-      const int r0 = 64 * wave + 16 * (i - 4), row = r0 + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
-      const uint16_t* g = a.vt + ((vt0 + jb) * kAD + row) * kFB + 8 * c;
-      dma16(g, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)(sV[st] + r0 * kFB)));
-    }
+    const int f = 4 * wave + (i & 3);
+    const uint16_t* g = (i < 4 ? a.k_pad : a.vt) + (tile0 + jb) * (kFB * kAD) + 512 * f;
+    dma16(wave_uniform(g), 16 * lane, (i < 4 ? ldsK : ldsV) + (uint32_t)(st * kFB * kAD + 512 * f) * 2);
   };
-  // scores of block jb: K fragments read two key steps ahead of their MFMAs
   auto scores = [&](int jb, f32x16& s) {
-    const uint16_t* K = sK[jb % kStg];
-    const int row = lane & 31;
-    auto kfrag = [&](int ks) { return lds_frag(K, row, kAD / 8, (2 * ks + (lane >> 5)) ^ (row & 15)); };
+    const uint16_t* K = sK[jb % kStg] + 8 * lane;
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = 0.f;
-    bf16x8 kr[3];
-    kr[0] = kfrag(0);
-    kr[1] = kfrag(1);
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      if (ks + 2 < 16) kr[(ks + 2) % 3] = kfrag(ks + 2);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[ks % 3], qf[ks], s, 0, 0, 0);
+    for (int ks = 0; ks < 16; ++ks)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(K + 512 * ks), qf[ks], s, 0, 0, 0);
+  };
+  // mask block jb's (unscaled) scores in place and update the running
+  // maximum; any_grow and alpha say whether and by how much O and lsum are
+  // rescaled (lsum here, O before the block's value product)
+  bool any_grow = false;
+  float alpha = 1.f;
+  auto mask_max = [&](int jb, f32x16& s) {
+    const int lim = my_q - kFB * jb - 4 * (lane >> 5);  // largest key offset 8 (r / 4) + r % 4 this lane sees
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = 8 * (r >> 2) + (r & 3) <= lim ? s[r] : -INFINITY;
+      s[r] = v;
+      bmax = fmaxf(bmax, v);
     }
+    // lanes l and l ^ 32 hold the two halves of the query's keys
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+    bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.scale_log2;
+    const bool grow = bmax > mrun + kRescale;
+    any_grow = __builtin_amdgcn_ballot_w64(grow) != 0;
+    const float mnew = grow ? bmax : mrun;
+    alpha = __builtin_amdgcn_exp2f(mrun - mnew);  // 1 where the maximum stays; 0 at the first block
+    if (any_grow) lsum *= alpha;
+    mrun = mnew;
   };
 
 #pragma unroll
@@ -389,64 +422,53 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(FwdArgs a) {
   __syncthreads();
   f32x16 sc;
   scores(0, sc);
+  mask_max(0, sc);
 
   for (int j = 0; j < nkb; ++j) {
     wait_vm8();      // this wave's copy of block j+1 has landed (j+2 may be in flight)
     __syncthreads(); // ... and every wave's; every wave is done with block j-1's stage
-    // (unconditional, so the scheduler can interleave these MFMAs with the
-    // softmax below; after the last block it scores a clamped block that is
-    // never used)
+    // (unconditional, so that these MFMAs share a basic block with the
+    // exponentials below; after the last block it scores a clamped block
+    // that is never used)
     f32x16 sn;
     scores(min(j + 1, nkb - 1), sn);
 #pragma unroll
     for (int i = 0; i < 4; ++i) copy_piece(j + kStg - 1, i);
-    // mask and online softmax (base 2) of block j
-    const int kb0 = kFB * j;
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kb0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const float v = key <= my_q ? sc[r] * a.scale_log2 : -INFINITY;
-      sc[r] = v;
-      bmax = fmaxf(bmax, v);
-    }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    const bool grow = bmax > mrun + kRescale;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float mnew = grow ? bmax : mrun;
-      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);  // mrun = -inf at first: 0
-      lsum *= alpha;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-      mrun = mnew;
-    }
     bf16x8 pf[2];
 #pragma unroll
     for (int uu = 0; uu < 2; ++uu) {
       u16x8 pk;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sc[8 * uu + e] - mrun);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * uu + e], a.scale_log2, -mrun));
         lsum += p;
         pk[e] = f32_to_bf16(p);
       }
       pf[uu] = __builtin_bit_cast(bf16x8, pk);
     }
+    // keep the exponentials in this basic block, beside the score MFMAs (the
+    // compiler would otherwise sink them past the rescale branch)
+    asm volatile("" : "+v"(pf[0]), "+v"(pf[1]), "+v"(lsum));
+    if (any_grow) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+    }
     // O^T += V^T P^T: 8 dim tiles, 2 steps of 16 keys; the other half of
     // the copy goes out between them
-    const uint16_t* V = sV[j % kStg];
+    const uint16_t* V = sV[j % kStg] + 8 * lane;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int row = 32 * dt + (lane & 31);
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const int c = (2 * g + (lane >> 5)) ^ ((row >> 2) & 3);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_frag(V, row, kFB / 8, c), pf[g], o[dt], 0, 0, 0);
-      }
+      for (int g = 0; g < 2; ++g)
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(V + 512 * (2 * dt + g)), pf[g],
+                                                        o[dt], 0, 0, 0);
       if (dt & 1) copy_piece(j + kStg - 1, 4 + (dt >> 1));
     }
+    // the next block's mask and maximum (a block past the last is wholly
+    // masked, so the final call changes nothing)
+    mask_max(j + 1, sn);
     sc = sn;
   }
   wait_vm0();
@@ -768,6 +790,7 @@ hipError_t launch_attn_prefill(const AttnArgs& a, void* ws, hipStream_t st) {
   pa.Hq = a.Hq;
   pa.Hk = a.Hk;
   pa.cache_len = a.cache_len;
+  pa.kblocks = tpad / kFB;
   pa.eps = a.eps;
   pa.base = a.rope_base;
   hipLaunchKernelGGL(attn_prep_kernel, dim3((unsigned)T), dim3(256), 0, st, pa);
