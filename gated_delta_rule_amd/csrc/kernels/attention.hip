@@ -157,7 +157,7 @@ __device__ __forceinline__ size_t vc_index(int n, int h, int Hk, int cache_len, 
 
 __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
   __shared__ float s_cos[kRot / 2], s_sin[kRot / 2];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = blockIdx.x;
   int n, pos;
   if (a.cu) {
@@ -167,6 +167,19 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
     n = t;
     pos = a.cache_lens[t];
   }
+  // rows hh = wave + 4 k of this token (q heads, then k heads), up to 8 per
+  // wave and pass; a pass loads all of its rows before it uses any, and the
+  // first pass's loads go out before the rotary angles are formed
+  const int rows = a.Hq + a.Hk;
+  auto row_src = [&](int hh) {
+    return hh < a.Hq ? a.q + ((size_t)t * a.Hq + hh) * kAD : a.k + ((size_t)t * a.Hk + (hh - a.Hq)) * kAD;
+  };
+  constexpr int kRowsPerPass = 8;
+  // (rows past the last are clamped to it: loaded, never used)
+  u16x4 raw[kRowsPerPass];
+#pragma unroll
+  for (int k = 0; k < kRowsPerPass; ++k)
+    raw[k] = *reinterpret_cast<const u16x4*>(row_src(min(wave + 4 * k, rows - 1)) + 4 * lane);
   if (tid < kRot / 2) {
     // angle pos * base^(-2j/64) in fp64, reduced to [-pi, pi] before the
     // fp32 sine and cosine, so large positions keep their accuracy
@@ -180,54 +193,62 @@ __global__ __launch_bounds__(256) void attn_prep_kernel(PrepArgs a) {
   __syncthreads();
   // a decode row whose position lies outside the cache is a padding row: no cache write
   const bool to_cache = a.k_cache && pos >= 0 && pos < a.cache_len;
-  for (int hh = wave; hh < a.Hq + a.Hk; hh += 4) {
-    const bool is_q = hh < a.Hq;
-    const int h = is_q ? hh : hh - a.Hq;
-    const uint16_t* src = is_q ? a.q + ((size_t)t * a.Hq + h) * kAD : a.k + ((size_t)t * a.Hk + h) * kAD;
-    const u16x4 raw = *reinterpret_cast<const u16x4*>(src + 4 * lane);
-    float x[4];
+  for (int h0 = wave; h0 < rows; h0 += 4 * kRowsPerPass) {
+    if (h0 != wave) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = bf16_to_f32(raw[e]);
-    float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-    ss = group_sum<64>(ss);
-    const float rn = 1.f / sqrtf(ss / kAD + a.eps);
-    const float* w = is_q ? a.q_w : a.k_w;
-    const f32x4 wv = *reinterpret_cast<const f32x4*>(w + 4 * lane);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = x[e] * rn * wv[e];
-    // rotation: lanes 0..7 hold dims 0..31 (first of each pair), lanes
-    // 8..15 dims 32..63 (second); partner lane l ^ 8
-    float y[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float o = __shfl_xor(x[e], 8, 64);
-      y[e] = x[e];
-      if (lane < 8) {
-        const int j = 4 * lane + e;
-        y[e] = x[e] * s_cos[j] - o * s_sin[j];
-      } else if (lane < 16) {
-        const int j = 4 * (lane - 8) + e;
-        y[e] = x[e] * s_cos[j] + o * s_sin[j];
-      }
+      for (int k = 0; k < kRowsPerPass; ++k)
+        raw[k] = *reinterpret_cast<const u16x4*>(row_src(min(h0 + 4 * k, rows - 1)) + 4 * lane);
     }
-    const u32x2 out = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-    if (is_q) {
-      *reinterpret_cast<u32x2*>(a.q_rot + ((size_t)t * a.Hq + h) * kAD + 4 * lane) = out;
-    } else {
-      if (a.k_pad) {
-        const size_t tp = (size_t)kKB * a.table[n] + pos;
-        *reinterpret_cast<u32x2*>(a.k_pad + kfrag_index(h, a.kblocks, (int64_t)tp, 4 * lane)) = out;
-      }
-      if (a.k_rot) *reinterpret_cast<u32x2*>(a.k_rot + ((size_t)t * a.Hk + h) * kAD + 4 * lane) = out;
-      if (to_cache) {
-        const size_t c = ((size_t)n * a.cache_len + pos) * a.Hk + h;
-        *reinterpret_cast<u32x2*>(a.k_cache + c * kAD + 4 * lane) = out;
-        if (!a.cu) {
-          // decode: the token's v into the blocked cache, one key column
-          const u16x4 vv = *reinterpret_cast<const u16x4*>(a.v + ((size_t)t * a.Hk + h) * kAD + 4 * lane);
-          uint16_t* vc = a.v_cache + vc_index(n, h, a.Hk, a.cache_len, 4 * lane, pos);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) vc[32 * e] = vv[e];
+    for (int k = 0; k < kRowsPerPass; ++k) {
+      const int hh = h0 + 4 * k;
+      if (hh >= rows) break;
+      const bool is_q = hh < a.Hq;
+      const int h = is_q ? hh : hh - a.Hq;
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = bf16_to_f32(raw[k][e]);
+      float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+      ss = group_sum<64>(ss);
+      const float rn = 1.f / sqrtf(ss / kAD + a.eps);
+      const float* w = is_q ? a.q_w : a.k_w;
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(w + 4 * lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = x[e] * rn * wv[e];
+      // rotation: lanes 0..7 hold dims 0..31 (first of each pair), lanes
+      // 8..15 dims 32..63 (second); partner lane l ^ 8
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float o = __shfl_xor(x[e], 8, 64);
+        y[e] = x[e];
+        if (lane < 8) {
+          const int j = 4 * lane + e;
+          y[e] = x[e] * s_cos[j] - o * s_sin[j];
+        } else if (lane < 16) {
+          const int j = 4 * (lane - 8) + e;
+          y[e] = x[e] * s_cos[j] + o * s_sin[j];
+        }
+      }
+      const u32x2 out = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+      if (is_q) {
+        *reinterpret_cast<u32x2*>(a.q_rot + ((size_t)t * a.Hq + h) * kAD + 4 * lane) = out;
+      } else {
+        if (a.k_pad) {
+          const size_t tp = (size_t)kKB * a.table[n] + pos;
+          *reinterpret_cast<u32x2*>(a.k_pad + kfrag_index(h, a.kblocks, (int64_t)tp, 4 * lane)) = out;
+        }
+        if (a.k_rot) *reinterpret_cast<u32x2*>(a.k_rot + ((size_t)t * a.Hk + h) * kAD + 4 * lane) = out;
+        if (to_cache) {
+          const size_t c = ((size_t)n * a.cache_len + pos) * a.Hk + h;
+          *reinterpret_cast<u32x2*>(a.k_cache + c * kAD + 4 * lane) = out;
+          if (!a.cu) {
+            // decode: the token's v into the blocked cache, one key column
+            const u16x4 vv = *reinterpret_cast<const u16x4*>(a.v + ((size_t)t * a.Hk + h) * kAD + 4 * lane);
+            uint16_t* vc = a.v_cache + vc_index(n, h, a.Hk, a.cache_len, 4 * lane, pos);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vc[32 * e] = vv[e];
+          }
         }
       }
     }
