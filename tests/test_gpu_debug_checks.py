@@ -117,3 +117,26 @@ def test_conv_debug_mode():
         bad = to_dev(np.asarray([0, 80, 70], np.int32), "i32", dev)
         _expect_invalid(lambda: gdr_amd.conv_gate_fused(bf(p.x), bf(p.conv_w), bad, f32(p.a), f32(p.b),
                                                         f32(p.A_log), f32(p.dt_bias), p.hk, p.hv, p.d), "decreases")
+
+
+def test_attn_prefill_debug_mode_bit_identical():
+    """The attention prefill's workspace (q', the padded keys and V^T) filled
+    with NaN first: keys past a sequence's end are never written, so the
+    output staying bit-identical shows the mask keeps them out of every
+    score, maximum and sum."""
+    import torch
+    import gated_delta_rule_amd as gdr_amd
+    dev = gpu()
+    lengths = (1, 63, 64, 65, 0, 129, 31)
+    x = synth.attn_inputs(83, lengths=lengths, hq=8, hk=2)
+    bf = lambda a: to_dev(a, "bf16", dev)
+    f32 = lambda a: to_dev(a, "f32", dev)
+    cu = to_dev(x.cu_seqlens.astype(np.int32), "i32", dev)
+    args = (bf(x.q), bf(x.k), bf(x.v), bf(x.gate), f32(x.q_norm_w), f32(x.k_norm_w), cu)
+    say(f"debug checks: attention prefill lengths {lengths}")
+    ref = gdr_amd.attn_prefill(*args)
+    with debug_checks():
+        out = gdr_amd.attn_prefill(*args)
+        torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    assert bits_equal(out, ref)
