@@ -74,6 +74,13 @@ __device__ __forceinline__ int perm32(int x) {
 __device__ __forceinline__ int perm8(int b) {
   return 32 * (b >> 2) + ((0x14041000u >> (8 * (b & 3))) & 0xff);
 }
+// Index of the first f32x4 piece of row r (1..15) of a 16x16 lower
+// triangle read row by row, pieces m4 = 0, 4, .. < r.
+__host__ __device__ constexpr int piece_base(int r) {
+  int n = 0;
+  for (int i = 1; i < r; ++i) n += (i + 3) / 4;
+  return n;
+}
 // Element offset of (row i, physical column p) in a compact T/P matrix: rows
 // 0..31 hold 32 columns (four 16-byte slots), rows 32..63 all 64 (eight);
 // slot s of row i is stored at s ^ ((i >> 1) & 3), resp. s ^ (i & 7), so
@@ -439,13 +446,25 @@ __global__ __launch_bounds__(kNT, 4) void chunk_prep_kernel(ChunkArgs a, unsigne
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+      // the 36 f32x4 pieces of the block's lower triangle (row r: m4 < r),
+      // in order, each read one piece before its use (two or more ahead
+      // spill under this kernel's 128-register budget)
+      constexpr int kAhead = 1;
+      constexpr int kPr[36] = {1, 2, 3, 4, 5, 5, 6, 6, 7, 7, 8, 8, 9, 9, 9, 10, 10, 10, 11, 11, 11, 12, 12, 12, 13, 13, 13, 13, 14, 14, 14, 14, 15, 15, 15, 15};
+      constexpr int kPm[36] = {0, 0, 0, 0, 0, 4, 0, 4, 0, 4, 0, 4, 0, 4, 8, 0, 4, 8, 0, 4, 8, 0, 4, 8, 0, 4, 8, 12, 0, 4, 8, 12, 0, 4, 8, 12};
+      f32x4 ring[kAhead + 1];
+#pragma unroll
+      for (int q = 0; q < kAhead; ++q) ring[q] = *reinterpret_cast<const f32x4*>(&sm.A[16 * b + kPr[q]][16 * b + kPm[q]]);
 #pragma unroll
       for (int r = 1; r < 16; ++r) {
-        const float* arow = &sm.A[16 * b + r][16 * b];
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int m4 = 0; m4 < r; m4 += 4) {
-          const f32x4 av = *reinterpret_cast<const f32x4*>(arow + m4);
+          const int q = piece_base(r) + m4 / 4;
+          if (q + kAhead < 36)
+            ring[(q + kAhead) % (kAhead + 1)] =
+                *reinterpret_cast<const f32x4*>(&sm.A[16 * b + kPr[q + kAhead]][16 * b + kPm[q + kAhead]]);
+          const f32x4 av = ring[q % (kAhead + 1)];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (m4 + e < r) {
